@@ -1,0 +1,158 @@
+"""fp64 CPU oracle for the S6 selective scan -- test infrastructure, not product code.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import this package.
+The product path (``selective_state_space_57_amd``) never imports it, and it imports nothing from the product.
+
+The arithmetic lives in ``oracle_scan.c`` (plain sequential recurrence in fp64, OpenMP over channels); this module
+only compiles it with gcc and marshals numpy arrays.  What it computes, with the passages it follows, is stated in the
+C file's header: the per-channel diagonal SSM of the Mamba paper (arXiv 2312.00752, sections 2-3, in the gitcode.csdn.net
+translation) with softplus Delta, exp(Delta*A) for A, the Euler rule Delta*B (default) or zero-order hold for B,
+y = C h + D x and the optional SiLU gate of the Mamba block (ifdog.com tutorial, "Mamba 架构").
+
+Pins (tests/test_oracle_pins.py) tie it to closed forms: the LTI convolution kernel, Theorem 1's gated RNN, the
+cumulative-sum (materialised) form, tree scans with the associative combine, split-sequence hand-off, linearity,
+reset/hold limits, the ZOH-to-Euler ratio and decode == scan.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_scan.c")
+_LIB = os.path.join(_HERE, "liboracle_scan.so")
+_lib = None
+
+EULER_B = 0
+ZOH = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no -ffast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-std=c11",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.oracle_scan_f64.argtypes = [I64, I64, I64, I64, I, I] + [P] * 11 + [I]
+    lib.oracle_scan_f64.restype = I
+    lib.oracle_state_update_f64.argtypes = [I64, I64, I64, I, I] + [P] * 10 + [I]
+    lib.oracle_state_update_f64.restype = I
+    lib.oracle_max_threads.restype = I
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def scan(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, disc=EULER_B, softplus=True, nthreads=0,
+         _lib_override=None):
+    """Full-sequence scan.  x, dt, z: (b, D, L); B, C: (b, N, L); A: (D, N); dt_bias, Dskip: (D,); h0: (b, D, N).
+
+    Returns (y (b, D, L), h_final (b, D, N)) as float64 arrays.
+    """
+    x = _f64(x)
+    bsz, dim, L = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _f64(dt, (bsz, dim, L))
+    A = _f64(A, (dim, N))
+    B = _f64(B, (bsz, N, L))
+    C = _f64(C, (bsz, N, L))
+    dt_bias = _f64(dt_bias, (dim,))
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, (bsz, dim, L))
+    h0 = _f64(h0, (bsz, dim, N))
+    y = np.empty((bsz, dim, L), np.float64)
+    hf = np.empty((bsz, dim, N), np.float64)
+    rc = (_lib_override or _load()).oracle_scan_f64(bsz, dim, L, N, int(disc), int(bool(softplus)), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                                 _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf),
+                                 int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_scan_f64 failed with code %d" % rc)
+    return y, hf
+
+
+def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, disc=EULER_B, softplus=True, nthreads=0,
+                 _lib_override=None):
+    """One decode step.  state: (b, D, N) (a copy is updated and returned); x, dt, z: (b, D); B, C: (b, N).
+
+    Returns (y (b, D), new_state (b, D, N)).
+    """
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    bsz, dim, N = st.shape
+    x = _f64(x, (bsz, dim))
+    dt = _f64(dt, (bsz, dim))
+    A = _f64(A, (dim, N))
+    B = _f64(B, (bsz, N))
+    C = _f64(C, (bsz, N))
+    dt_bias = _f64(dt_bias, (dim,))
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, (bsz, dim))
+    y = np.empty((bsz, dim), np.float64)
+    rc = (_lib_override or _load()).oracle_state_update_f64(bsz, dim, N, int(disc), int(bool(softplus)), _ptr(st), _ptr(x), _ptr(dt),
+                                         _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y),
+                                         int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_state_update_f64 failed with code %d" % rc)
+    return y, st
+
+
+class Oracle:
+    """The oracle bound to a specific compiled library (the default one, or a test-built variant)."""
+
+    def __init__(self, libpath: str | None = None):
+        self._lib = _bind(libpath) if libpath else None
+
+    def scan(self, *a, **k):
+        return scan(*a, _lib_override=self._lib, **k)
+
+    def state_update(self, *a, **k):
+        return state_update(*a, _lib_override=self._lib, **k)
+
+
+def compile_variant(src_text: str, out_path: str) -> str:
+    """Compile a variant of the oracle source text (used by the mutation test to plant mistakes)."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-std=c11", src, "-o",
+                           out_path, "-lm"])
+    return out_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()

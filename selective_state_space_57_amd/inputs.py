@@ -1,0 +1,183 @@
+"""Seeded synthetic inputs for the selective scan (shared by the tests, the benchmark and the oracle's callers).
+
+This module holds no part of the scan's arithmetic: it draws random numbers, rounds them to the storage dtype and
+converts storage formats.  Nothing here imports the HIP binding or the oracle.
+
+Workloads (sizes b, D, L, N) follow the Mamba paper's settings: N = 16 states per channel (paper section 4.5/4.6
+ablations, state dimension 16), d_inner = E * d_model with E = 2 (section 3.4), layer shapes of the 130M and 2.8B
+models, million-length sequences as in the DNA and audio experiments (sections 4.3-4.4), and large-batch recurrent
+decode (section 4.5).  Initialisations follow section 3.6: A from S4D-Real, A_n = -(n+1), and the Delta bias drawn as
+softplus^-1 of a value log-uniform in a range around [0.001, 0.1].
+
+Recipe (also written out in the design doc):
+  * every tensor k of workload `cfg` at decode step `step` is drawn in flattened chunks of 2**24 elements, chunk i
+    from numpy's default_rng(SeedSequence(57, spawn_key=(cfg, step, k, i)));
+  * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state;
+  * normals are numpy float32 standard normals; log-uniforms are exp(uniform(log lo, log hi)) in float64;
+  * Delta-logit = softplus^-1(Delta*) - bias[d], with softplus^-1(v) = log(expm1(v)), rounded to the io dtype;
+  * bf16 values are rounded to nearest-even from float32 (float64 -> float32 -> bf16 for float64 sources).
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+CHUNK = 1 << 24
+SEED = 57
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    io: str                 # "f32" or "bf16" for x, dt, B, C, z (and y)
+    delta_lo: float
+    delta_hi: float
+    a_jitter: float         # std of the N(0, s) jitter added to A = -(n+1); 0 = exact S4D-Real
+    gate: bool = True
+    dskip: bool = True
+    decode_steps: int = 0   # > 0: single-token decode workload, seqlen ignored
+    cfg_id: int = 0
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    0: Workload("tiny-s6-fp32", 1, 64, 256, 16, F32, 1e-3, 1e-1, 0.0, cfg_id=0),
+    1: Workload("mamba130m-layer", 8, 1536, 2048, 16, BF16, 1e-3, 1e-1, 0.1, cfg_id=1),
+    2: Workload("mamba2.8b-layer", 4, 5120, 4096, 16, BF16, 1e-3, 1e-1, 0.1, cfg_id=2),
+    3: Workload("million-length", 1, 512, 1 << 20, 16, BF16, 1e-4, 1e-1, 0.1, cfg_id=3),
+    4: Workload("decode-b256-d5120", 256, 5120, 1, 16, BF16, 1e-3, 1e-1, 0.1, decode_steps=64, cfg_id=4),
+}
+
+
+def _rng(cfg: int, step: int, k: int, i: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(cfg, step, k, i)))
+
+
+def _normal(cfg, step, k, n) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    for i, s in enumerate(range(0, n, CHUNK)):
+        e = min(n, s + CHUNK)
+        out[s:e] = _rng(cfg, step, k, i).standard_normal(e - s, dtype=np.float32)
+    return out
+
+
+def _loguniform(cfg, step, k, n, lo, hi) -> np.ndarray:
+    out = np.empty(n, np.float64)
+    llo, lhi = np.log(lo), np.log(hi)
+    for i, s in enumerate(range(0, n, CHUNK)):
+        e = min(n, s + CHUNK)
+        out[s:e] = np.exp(_rng(cfg, step, k, i).uniform(llo, lhi, e - s))
+    return out
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest-even), returned as uint16 bit patterns.  Finite inputs only."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_storage(a: np.ndarray, io: str) -> np.ndarray:
+    """float32/float64 values -> storage array (float32, or uint16 bf16 bits)."""
+    a32 = np.asarray(a, dtype=np.float32)
+    return f32_to_bf16_bits(a32) if io == BF16 else np.ascontiguousarray(a32)
+
+
+def to_f64(a: np.ndarray, io: str | None = None) -> np.ndarray:
+    """Storage array -> exact float64 values."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def _softplus_inv(v: np.ndarray) -> np.ndarray:
+    # inverse of log(1 + e^u): u = log(e^v - 1); used only to place the drawn Delta values, not part of the scan
+    return np.log(np.expm1(v))
+
+
+def scan_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
+    """Inputs for ssm_scan_fwd (or one decode step when w.decode_steps > 0, with seqlen = 1 squeezed away).
+
+    Returns a dict of storage arrays: x, dt, z (b, D, L); B, C (b, N, L); A (D, N) f32; dt_bias, Dskip (D,) f32;
+    h0 (b, D, N) f32 or None.  For decode workloads the sequence tensors are (b, D) and (b, N).
+    """
+    b, D, N = w.batch, w.dim, w.dstate
+    L = 1 if w.decode_steps else w.seqlen
+    c = w.cfg_id
+    nx = b * D * L
+    x = _normal(c, step, 0, nx)
+    delta = _loguniform(c, step, 1, nx, w.delta_lo, w.delta_hi)
+    # the bias is a per-channel parameter: drawn once (decode step 0) and reused by every step
+    bias = _softplus_inv(_loguniform(c, 0, 2, D, w.delta_lo, w.delta_hi)).astype(np.float32)
+    base = -(np.arange(N, dtype=np.float64) + 1.0)
+    if w.a_jitter > 0:
+        jit = _normal(c, 0, 3, D * N).astype(np.float64).reshape(D, N) * w.a_jitter
+        A = np.minimum(base[None, :] + jit, -1e-4)
+    else:
+        A = np.broadcast_to(base, (D, N)).copy()
+    A = A.astype(np.float32)
+    Bm = _normal(c, step, 4, b * N * L)
+    Cm = _normal(c, step, 5, b * N * L)
+    Dskip = _normal(c, 0, 6, D) if w.dskip else None
+    z = _normal(c, step, 7, nx) if w.gate else None
+    logit = (_softplus_inv(delta).reshape(b, D, L) - bias.astype(np.float64)[None, :, None]).reshape(-1)
+    io = w.io
+    shp = (b, D) if w.decode_steps else (b, D, L)
+    bshp = (b, N) if w.decode_steps else (b, N, L)
+    out = {
+        "x": to_storage(x, io).reshape(shp),
+        "dt": to_storage(logit, io).reshape(shp),
+        "dt_bias": bias,
+        "A": A,
+        "B": to_storage(Bm, io).reshape(bshp),
+        "C": to_storage(Cm, io).reshape(bshp),
+        "Dskip": None if Dskip is None else Dskip.astype(np.float32),
+        "z": None if z is None else to_storage(z, io).reshape(shp),
+        "h0": None,
+    }
+    if with_h0:
+        out["h0"] = _normal(c, 0, 8, b * D * N).reshape(b, D, N)
+    return out
+
+
+def decode_state(w: Workload) -> np.ndarray:
+    """Initial decode state (b, D, N) f32, N(0, 1)."""
+    return _normal(w.cfg_id, 0, 8, w.batch * w.dim * w.dstate).reshape(w.batch, w.dim, w.dstate)
+
+
+def random_small(seed: int, b: int, D: int, L: int, N: int, io: str = F32, delta=(1e-3, 1e-1), a_jitter=0.1,
+                 gate=True, dskip=True, bias=True, h0=False) -> dict:
+    """Small random case for parity sweeps (odd sizes, optional parts switched off)."""
+    w = Workload("small", b, D, L, N, io, delta[0], delta[1], a_jitter, gate, dskip, cfg_id=1000 + seed)
+    d = scan_inputs(w, with_h0=h0)
+    if not bias:
+        # fold the bias into the logit so that the same Delta values are produced without a bias vector
+        lg = to_f64(d["dt"]) + d["dt_bias"].astype(np.float64)[None, :, None]
+        d["dt"] = to_storage(lg, io)
+        d["dt_bias"] = None
+    return d
+
+
+def as_f64(d: dict) -> dict:
+    """Storage dict -> float64 dict for the oracle."""
+    return {k: (None if v is None else to_f64(v)) for k, v in d.items()}

@@ -1,0 +1,311 @@
+"""Independent checks that pin the fp64 oracle to what the pages and the mathematics fix.
+
+Each check takes an oracle object (``oracle.Oracle``) and raises AssertionError on disagreement.  None of them
+re-types the oracle's step loop: each computes the expected value by a different route (a convolution kernel, a
+gated RNN, cumulative sums, a tree scan, a hand-worked example, an algebraic identity).
+
+Sources (cited by page title and section):
+  * Mamba paper (arXiv 2312.00752), Chinese translation on gitcode.csdn.net: section 2 (discretisation, recurrence
+    (2), convolution (3), LTI, diagonal structure), section 3.3.2 (scan), section 3.5 (Theorem 1, selection effects:
+    boundary reset with Delta -> inf, ignoring inputs with Delta -> 0), section 3.6 (S4D-Real A, Delta bias init).
+  * "Mamba" tutorial on docs.ifdog.com: sections on ZOH discretisation (diagonal case), S4's convolution view
+    (K = [CB, CAB, CA^2B, ...]), softplus, the associative combine of the parallel scan, SiLU gate of the block.
+  * Close reading on alishangtian.com: statement of Theorem 1 (N = 1, A = -1 gives a gated RNN).
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+EULER_B, ZOH = 0, 1
+
+
+def _rng(seed):
+    return np.random.default_rng(np.random.SeedSequence(5757, spawn_key=(seed,)))
+
+
+def _case(seed, b=2, D=3, L=23, N=4, gate=True, dskip=True, h0=True, drange=(1e-3, 1.5)):
+    r = _rng(seed)
+    x = r.standard_normal((b, D, L))
+    # logits whose softplus covers [drange]: u = log(expm1(delta))
+    delta = np.exp(r.uniform(np.log(drange[0]), np.log(drange[1]), (b, D, L)))
+    bias = r.uniform(-0.5, 0.5, D)
+    dt = np.log(np.expm1(delta)) - bias[None, :, None]
+    A = -(np.arange(N) + 1.0)[None, :] * np.exp(r.uniform(-0.3, 0.3, (D, N)))
+    B = r.standard_normal((b, N, L))
+    C = r.standard_normal((b, N, L))
+    Dk = r.standard_normal(D) if dskip else None
+    z = r.standard_normal((b, D, L)) if gate else None
+    H0 = r.standard_normal((b, D, N)) if h0 else None
+    return dict(x=x, dt=dt, dt_bias=bias, A=A, B=B, C=C, Dskip=Dk, z=z, h0=H0)
+
+
+def _softplus_lib(u):
+    # library route, independent of the oracle's max(u,0)+log1p(exp(-|u|)) form
+    return np.logaddexp(0.0, u)
+
+
+def _coef(delta, A, disc):
+    """B-bar / B for the two discretisation rules (tutorial ZOH formula, diagonal case; Euler = Delta)."""
+    if disc == EULER_B:
+        return delta
+    with np.errstate(invalid="ignore", divide="ignore"):
+        c = np.expm1(delta * A) / A
+    return np.where(A == 0.0, delta, c)
+
+
+def _silu(z):
+    return z * (1.0 / (1.0 + np.exp(-z)))
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(1e-300, float(np.max(np.abs(b)))))
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# P1: LTI case equals the convolution y = K * x with K_k = sum_n C_n Abar_n^k Bbar_n (+ D x)  (paper section 2,
+#     equations (2)-(3); tutorial "卷积视角与 FFT 并行").  Brute force O(L^2).
+def pin_lti_convolution(orc, disc, N=4, L=40, seed=1):
+    r = _rng(100 + seed + 10 * disc + N)
+    D = 3
+    u = r.uniform(-3, 1, D)                   # one Delta logit per channel, constant in time
+    A = -(np.arange(N) + 1.0)[None, :] * np.exp(r.uniform(-0.2, 0.2, (D, N)))
+    Bv = r.standard_normal(N)
+    Cv = r.standard_normal(N)
+    Dk = r.standard_normal(D)
+    x = r.standard_normal((1, D, L))
+    dt = np.repeat(u[None, :, None], L, axis=2)
+    Bm = np.repeat(Bv[None, :, None], L, axis=2)
+    Cm = np.repeat(Cv[None, :, None], L, axis=2)
+    y, _ = orc.scan(x, dt, A, Bm, Cm, Dskip=Dk, disc=disc)
+    delta = _softplus_lib(u)
+    exp_y = np.zeros((1, D, L))
+    for d in range(D):
+        Ab = np.exp(delta[d] * A[d])
+        Bb = _coef(delta[d], A[d], disc) * Bv
+        K = np.array([np.sum(Cv * Ab ** k * Bb) for k in range(L)])
+        exp_y[0, d] = np.convolve(x[0, d], K)[:L] + Dk[d] * x[0, d]
+    assert _rel(y, exp_y) < 1e-12, ("P1", disc, N, _rel(y, exp_y))
+
+
+# P2: Theorem 1 (paper section 3.5.1; alishangtian statement): N = 1, A = -1, B = C = 1, ZOH, Delta = softplus(u)
+#     gives h_t = (1 - g_t) h_{t-1} + g_t x_t with g_t = sigmoid(u_t).
+def pin_theorem1(orc, L=57, seed=2):
+    r = _rng(200 + seed)
+    D = 4
+    x = r.standard_normal((1, D, L))
+    u = r.uniform(-6, 6, (1, D, L))
+    h0 = r.standard_normal((1, D, 1))
+    y, hf = orc.scan(x, u, -np.ones((D, 1)), np.ones((1, 1, L)), np.ones((1, 1, L)), h0=h0, disc=ZOH)
+    g = 1.0 / (1.0 + np.exp(-u))
+    h = h0[0, :, 0].copy()
+    exp_y = np.zeros_like(x)
+    for t in range(L):
+        h = (1 - g[0, :, t]) * h + g[0, :, t] * x[0, :, t]
+        exp_y[0, :, t] = h
+    assert np.max(np.abs(y - exp_y)) < 1e-13 * max(1.0, np.max(np.abs(exp_y))), ("P2", np.max(np.abs(y - exp_y)))
+    assert np.max(np.abs(hf[0, :, 0] - h)) < 1e-13
+
+
+# P3: splitting the sequence and handing over the state equals the single pass (constant-size recurrent state,
+#     paper section 1 (ii)).
+def pin_split(orc, disc, seed=3):
+    c = _case(300 + seed + disc, L=37)
+    y, hf = orc.scan(**c, disc=disc)
+    cut = 1 + seed % 30
+    s1 = {k: (v[..., :cut] if k in ("x", "dt", "B", "C", "z") and v is not None else v) for k, v in c.items()}
+    s2 = {k: (v[..., cut:] if k in ("x", "dt", "B", "C", "z") and v is not None else v) for k, v in c.items()}
+    y1, h1 = orc.scan(**s1, disc=disc)
+    s2["h0"] = h1
+    y2, h2 = orc.scan(**s2, disc=disc)
+    assert _rel(np.concatenate([y1, y2], axis=2), y) < 1e-13, "P3 y"
+    assert _rel(h2, hf) < 1e-13, "P3 h_final"
+
+
+# P4: the materialised (cumulative-sum) form.  With S_t = sum_{r<=t} Delta_r,
+#     h_t,n = sum_{s<=t} exp(A_n (S_t - S_s)) Bbar_{s,n} x_s + exp(A_n S_t) h0_n   (the expanded state of shape
+#     (B, L, D, N) that paper section 3.3 describes and never materialises on the GPU).
+def pin_materialised(orc, disc, seed=4):
+    c = _case(400 + seed + disc, b=2, D=2, L=19, N=3)
+    y, hf = orc.scan(**c, disc=disc)
+    b, D, L = c["x"].shape
+    N = c["A"].shape[1]
+    delta = _softplus_lib(c["dt"] + c["dt_bias"][None, :, None])
+    S = np.cumsum(delta, axis=2)
+    exp_y = np.zeros_like(c["x"])
+    exp_h = np.zeros((b, D, N))
+    for bi in range(b):
+        for d in range(D):
+            A = c["A"][d]
+            H = np.zeros((L, N))
+            for t in range(L):
+                acc = np.exp(A * S[bi, d, t]) * c["h0"][bi, d]
+                for s in range(t + 1):
+                    bb = _coef(delta[bi, d, s], A, disc) * c["B"][bi, :, s] * c["x"][bi, d, s]
+                    acc = acc + np.exp(A * (S[bi, d, t] - S[bi, d, s])) * bb
+                H[t] = acc
+            yy = np.sum(c["C"][bi].T * H, axis=1) + c["Dskip"][d] * c["x"][bi, d]
+            exp_y[bi, d] = yy * _silu(c["z"][bi, d])
+            exp_h[bi, d] = H[-1]
+    assert _rel(y, exp_y) < 1e-10, ("P4 y", _rel(y, exp_y))
+    assert _rel(hf, exp_h) < 1e-10, ("P4 h", _rel(hf, exp_h))
+
+
+# P5: associativity.  The parallel scan's combine (a1, b1) o (a2, b2) = (a2 a1, a2 b1 + b2) (tutorial, "硬件感知的
+#     并行扫描"), applied as Hillis-Steele and as a chunked two-level scan, reproduces the oracle's states.
+def _combine(p, q):
+    return q[0] * p[0], q[0] * p[1] + q[1]
+
+
+def pin_associative(orc, disc, seed=5):
+    c = _case(500 + seed + disc, b=1, D=2, L=29, N=3, gate=False, dskip=False)
+    y, hf = orc.scan(**c, disc=disc)
+    delta = _softplus_lib(c["dt"] + c["dt_bias"][None, :, None])[0]
+    L = delta.shape[1]
+    for d in range(2):
+        A = c["A"][d]
+        a = np.exp(delta[d][:, None] * A[None, :])                                          # (L, N)
+        bb = _coef(delta[d][:, None], A[None, :], disc) * c["B"][0].T * c["x"][0, d][:, None]
+        # Hillis-Steele inclusive scan
+        pa, pb = a.copy(), bb.copy()
+        k = 1
+        while k < L:
+            na, nb = pa.copy(), pb.copy()
+            for t in range(k, L):
+                na[t], nb[t] = _combine((pa[t - k], pb[t - k]), (pa[t], pb[t]))
+            pa, pb = na, nb
+            k *= 2
+        H = pa * c["h0"][0, d][None, :] + pb
+        assert _rel(H[-1], hf[0, d]) < 1e-13, "P5 Hillis-Steele h_final"
+        assert _rel(np.sum(c["C"][0].T * H, axis=1), y[0, d]) < 1e-12, "P5 Hillis-Steele y"
+        # chunked: per-chunk aggregates, exclusive scan of aggregates, replay
+        cs = 1 + (seed + d) % 7
+        carry = (np.ones(a.shape[1]), c["h0"][0, d].copy())
+        H2 = np.zeros_like(H)
+        for s0 in range(0, L, cs):
+            agg = (np.ones(a.shape[1]), np.zeros(a.shape[1]))
+            for t in range(s0, min(L, s0 + cs)):
+                agg = _combine(agg, (a[t], bb[t]))
+                tot = _combine(carry, agg)
+                H2[t] = tot[1]
+            carry = _combine(carry, agg)
+        assert _rel(H2, H) < 1e-13, "P5 chunked"
+
+
+# P6: linearity in (x, h0) when Delta, B, C are fixed and the gate is off (recurrence (2) is linear).
+def pin_linearity(orc, disc, seed=6):
+    c1 = _case(600 + seed + disc, gate=False)
+    c2 = _case(650 + seed + disc, gate=False)
+    al, be = 0.7, -1.3
+    mix = dict(c1)
+    mix["x"] = al * c1["x"] + be * c2["x"]
+    mix["h0"] = al * c1["h0"] + be * c2["h0"]
+    c2s = dict(c1)
+    c2s["x"], c2s["h0"] = c2["x"], c2["h0"]
+    y1, h1 = orc.scan(**c1, disc=disc)
+    y2, h2 = orc.scan(**c2s, disc=disc)
+    ym, hm = orc.scan(**mix, disc=disc)
+    assert _rel(ym, al * y1 + be * y2) < 1e-12, "P6 y"
+    assert _rel(hm, al * h1 + be * h2) < 1e-12, "P6 h"
+
+
+# P7: selection effects (paper section 3.5.2): a huge Delta at t* resets the state, so outputs from t* on do not
+#     depend on anything before t*; a vanishing Delta keeps the state and ignores the input.
+def pin_reset_hold(orc, disc, seed=7):
+    c = _case(700 + seed + disc, L=30)
+    ts = 11
+    c["dt"] = c["dt"].copy()
+    c["dt"][:, :, ts] = 1e4
+    y, hf = orc.scan(**c, disc=disc)
+    c2 = dict(c)
+    r = _rng(750 + seed)
+    c2["x"] = c["x"].copy()
+    c2["x"][:, :, :ts] = r.standard_normal(c["x"][:, :, :ts].shape)
+    c2["h0"] = r.standard_normal(c["h0"].shape)
+    y2, hf2 = orc.scan(**c2, disc=disc)
+    assert np.array_equal(y[:, :, ts:], y2[:, :, ts:]), "P7 reset"
+    assert np.array_equal(hf, hf2), "P7 reset h"
+    assert not np.allclose(y[:, :, :ts], y2[:, :, :ts]), "P7 reset sanity"
+    # hold: Delta = 1e-12 (softplus off) => h ~ h0, y ~ (C.h0 + D x) silu(z)
+    c3 = dict(c)
+    c3["dt"] = np.full_like(c["dt"], 1e-12)
+    c3["dt_bias"] = None
+    y3, hf3 = orc.scan(**c3, disc=disc, softplus=False)
+    exp = (np.einsum("bnl,bdn->bdl", c["C"], c["h0"]) + c["Dskip"][None, :, None] * c["x"]) * _silu(c["z"])
+    assert np.max(np.abs(y3 - exp)) < 1e-9, "P7 hold y"
+    assert np.max(np.abs(hf3 - c["h0"])) < 1e-9, "P7 hold h"
+
+
+# P8: ZOH vs Euler for B: one step from h0 = 0 with x = B = C = 1 gives y_ZOH / y_Euler = expm1(Delta A)/(Delta A),
+#     which tends to 1 + Delta A / 2 as Delta -> 0 (tutorial ZOH formula, diagonal case).
+def pin_zoh_euler(orc):
+    for u, a in [(-8.0, -1.0), (-2.0, -3.5), (0.5, -0.25), (3.0, -16.0), (-20.0, -1.0)]:
+        args = (np.ones((1, 1, 1)), np.full((1, 1, 1), u), np.full((1, 1), a), np.ones((1, 1, 1)), np.ones((1, 1, 1)))
+        yz, _ = orc.scan(*args, disc=ZOH)
+        ye, _ = orc.scan(*args, disc=EULER_B)
+        delta = math.log1p(math.exp(u)) if u < 30 else u
+        ratio = math.expm1(delta * a) / (delta * a)
+        assert abs(yz[0, 0, 0] / ye[0, 0, 0] - ratio) < 1e-14, ("P8", u, a)
+        if delta < 1e-3:
+            assert abs(ratio - (1 + delta * a / 2)) < (delta * a) ** 2 + 4e-16
+    # A == 0 takes the limit Delta * B
+    args = (np.ones((1, 1, 1)), np.zeros((1, 1, 1)), np.zeros((1, 1)), np.ones((1, 1, 1)), np.ones((1, 1, 1)))
+    yz, _ = orc.scan(*args, disc=ZOH)
+    assert abs(yz[0, 0, 0] - math.log(2.0)) < 1e-15
+
+
+# P9: decode == scan: L single-token steps equal one scan of length L started from the same state.
+def pin_decode_scan(orc, disc, seed=9):
+    c = _case(900 + seed + disc, L=13)
+    y, hf = orc.scan(**c, disc=disc)
+    st = c["h0"].copy()
+    for t in range(c["x"].shape[2]):
+        yt, st = orc.state_update(st, c["x"][:, :, t], c["dt"][:, :, t], c["A"], c["B"][:, :, t], c["C"][:, :, t],
+                                  dt_bias=c["dt_bias"], Dskip=c["Dskip"], z=c["z"][:, :, t], disc=disc)
+        assert _rel(yt, y[:, :, t]) < 1e-14, "P9 y"
+    assert _rel(st, hf) < 1e-14, "P9 state"
+    # decode reduces to Theorem 1's gated RNN as well (independent of the scan entry point)
+    r = _rng(990 + seed)
+    u = r.uniform(-5, 5, (1, 3))
+    xv = r.standard_normal((1, 3))
+    s0 = r.standard_normal((1, 3, 1))
+    yd, s1 = orc.state_update(s0, xv, u, -np.ones((3, 1)), np.ones((1, 1)), np.ones((1, 1)), disc=ZOH)
+    g = 1 / (1 + np.exp(-u))
+    assert np.max(np.abs(yd - ((1 - g) * s0[:, :, 0] + g * xv))) < 1e-14, "P9 theorem-1 decode"
+
+
+# Worked examples computed by hand from the definitions (tests/golden/worked_examples.txt).
+def pin_worked_examples(orc, rows):
+    for row in rows:
+        disc = EULER_B if row["disc"] == "euler" else ZOH
+        N = 1
+        args = dict(x=np.full((1, 1, 1), row["x"]), dt=np.full((1, 1, 1), row["u"]), A=np.full((1, N), row["A"]),
+                    B=np.full((1, N, 1), row["B"]), C=np.full((1, N, 1), row["C"]),
+                    Dskip=None if row["D"] is None else np.array([row["D"]]),
+                    z=None if row["z"] is None else np.full((1, 1, 1), row["z"]), h0=np.full((1, 1, N), row["h0"]))
+        y, hf = orc.scan(**args, disc=disc)
+        assert abs(y[0, 0, 0] - row["y"]) < 1e-14 * max(1, abs(row["y"])), (row["name"], y[0, 0, 0], row["y"])
+        assert abs(hf[0, 0, 0] - row["h"]) < 1e-14 * max(1, abs(row["h"])), (row["name"], hf[0, 0, 0], row["h"])
+
+
+def all_pins(orc, worked_rows):
+    """Run every pin; returns a list of (name, error-or-None)."""
+    out = []
+    checks = [("worked", lambda: pin_worked_examples(orc, worked_rows)), ("theorem1", lambda: pin_theorem1(orc)),
+              ("zoh_euler", lambda: pin_zoh_euler(orc))]
+    for disc in (EULER_B, ZOH):
+        for N in (1, 4, 16):
+            checks.append(("lti_N%d_disc%d" % (N, disc), lambda disc=disc, N=N: pin_lti_convolution(orc, disc, N=N)))
+        checks += [("split_%d" % disc, lambda disc=disc: pin_split(orc, disc)),
+                   ("materialised_%d" % disc, lambda disc=disc: pin_materialised(orc, disc)),
+                   ("associative_%d" % disc, lambda disc=disc: pin_associative(orc, disc)),
+                   ("linearity_%d" % disc, lambda disc=disc: pin_linearity(orc, disc)),
+                   ("reset_hold_%d" % disc, lambda disc=disc: pin_reset_hold(orc, disc)),
+                   ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc))]
+    for name, fn in checks:
+        try:
+            fn()
+            out.append((name, None))
+        except Exception as e:  # noqa: BLE001 -- a mutant may also crash or raise
+            out.append((name, repr(e)[:200]))
+    return out

@@ -1,0 +1,103 @@
+"""CPU tests: the fp64 oracle against its pins (closed forms, identities, hand-worked examples), and a mutation
+test showing that plausible mistakes planted in the oracle's source are caught by at least one pin."""
+import os
+import re
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.txt")
+
+
+def load_worked():
+    rows = []
+    for line in open(GOLDEN):
+        if not line.strip() or line.startswith("#"):
+            continue
+        f = line.split()
+        num = lambda s: None if s == "-" else float(s)
+        rows.append(dict(name=f[0], disc=f[1], u=num(f[2]), A=num(f[3]), B=num(f[4]), C=num(f[5]), x=num(f[6]),
+                         h0=num(f[7]), D=num(f[8]), z=num(f[9]), y=num(f[10]), h=num(f[11])))
+    return rows
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build(force=False)
+    return oracle.Oracle()
+
+
+def test_worked_examples(orc):
+    pins.pin_worked_examples(orc, load_worked())
+
+
+def test_theorem1(orc):
+    pins.pin_theorem1(orc)
+
+
+def test_zoh_euler_ratio(orc):
+    pins.pin_zoh_euler(orc)
+
+
+@pytest.mark.parametrize("disc", [pins.EULER_B, pins.ZOH])
+@pytest.mark.parametrize("N", [1, 4, 16])
+def test_lti_convolution(orc, disc, N):
+    pins.pin_lti_convolution(orc, disc, N=N)
+
+
+@pytest.mark.parametrize("disc", [pins.EULER_B, pins.ZOH])
+@pytest.mark.parametrize("name", ["split", "materialised", "associative", "linearity", "reset_hold", "decode_scan"])
+def test_identity(orc, name, disc):
+    getattr(pins, "pin_" + name)(orc, disc)
+
+
+def test_softplus_tails(orc):
+    # Delta for very negative / positive logits: log1p(e^u) ~ e^u and ~ u + e^-u (no cancellation, no overflow).
+    u = np.array([-40.0, -12.0, 0.0, 12.0, 40.0, 700.0])
+    x = np.ones((1, 1, 6))
+    # N = 1, A tiny so Abar ~ 1 and h after each step accumulates Delta; use one step per channel instead
+    for i, uu in enumerate(u):
+        y, _ = orc.scan(np.ones((1, 1, 1)), np.full((1, 1, 1), uu), np.full((1, 1), -1e-300), np.ones((1, 1, 1)),
+                        np.ones((1, 1, 1)))
+        exp = np.logaddexp(0.0, uu)
+        assert abs(y[0, 0, 0] - exp) <= 1e-15 * max(1.0, exp), (uu, y[0, 0, 0], exp)
+
+
+# Mutation test: each planted mistake is a regex substitution on oracle_scan.c; every mutant must fail a pin.
+MUTANTS = [
+    ("drop_dskip", r"if \(has_D\) y \+= Dv \* xv;", "if (has_D) y += 0.0 * xv;"),
+    ("gate_wrong_sign", r"zv / \(1\.0 \+ exp\(-zv\)\)", "zv / (1.0 + exp(zv))"),
+    ("abar_sign", r"exp\(delta \* An\)", "exp(-delta * An)"),
+    ("abar_missing_delta", r"double abar = exp\(delta \* An\);", "double abar = exp(An);"),
+    ("euler_no_delta", r"coef = delta;\n    \} else", "coef = 1.0;\n    } else"),
+    ("zoh_no_div", r"expm1\(delta \* An\) / An", "expm1(delta * An)"),
+    ("softplus_plain", r"return u > 0\.0 \? u \+ log1p\(exp\(-u\)\) : log1p\(exp\(u\)\);", "return u;"),
+    ("softplus_pos_branch", r"u \+ log1p\(exp\(-u\)\)", "log1p(exp(-u))"),
+    ("bias_ignored", r"double u = dtv \+ bias;", "double u = dtv;"),
+    ("y_before_update", r"h\[n\] = abar \* h\[n\] \+ coef \* Bt\[n \* Bstride\] \* xv;\n    y \+= Ct\[n \* Cstride\] \* h\[n\];",
+     "y += Ct[n * Cstride] * h[n];\n    h[n] = abar * h[n] + coef * Bt[n * Bstride] * xv;"),
+    ("B_C_swapped", r"coef \* Bt\[n \* Bstride\]", "coef * Ct[n * Cstride]"),
+    ("h0_ignored", r"h\[n\] = h0 \? h0\[ch \* dstate \+ n\] : 0\.0;", "h[n] = 0.0;"),
+    ("B_wrong_batch", r"const double\* Bb = B \+ b \* dstate \* seqlen;", "const double* Bb = B;"),
+    ("A_wrong_row", r"A \+ d \* dstate, Bb \+ t", "A, Bb + t"),
+    ("x_time_shift", r"yr\[t\] = step\(dstate, disc, use_softplus, xr\[t\]",
+     "yr[t] = step(dstate, disc, use_softplus, xr[t > 0 ? t - 1 : 0]"),
+    ("hfinal_zero", r"h_final\[ch \* dstate \+ n\] = h\[n\];", "h_final[ch * dstate + n] = 0.0;"),
+    ("decode_bias_ignored", r"dt\[ch\], dt_bias \? dt_bias\[d\] : 0\.0", "dt[ch], 0.0"),
+]
+
+
+@pytest.mark.parametrize("name,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, pat, rep):
+    src = oracle.source_text()
+    mutated, n = re.subn(pat, rep, src)
+    assert n >= 1, "mutation pattern %s no longer matches the oracle source" % name
+    with tempfile.TemporaryDirectory() as td:
+        lib = oracle.compile_variant(mutated, os.path.join(td, "mut_%s.so" % name))
+        res = pins.all_pins(oracle.Oracle(lib), load_worked())
+    failed = [k for k, e in res if e is not None]
+    assert failed, "mutant %s passed every pin" % name
