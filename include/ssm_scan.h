@@ -1,0 +1,120 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) S6 selective-scan library (libssm57.so).
+ *
+ * The operation (Mamba paper, arXiv 2312.00752, gitcode.csdn.net translation: section 2 "discretisation",
+ * "computation" and "structure and dimensions"; section 3.2 (s_B, s_C, s_Delta, tau_Delta = softplus); section 3.3.2
+ * (fused selective scan that never materialises the (B, L, D, N) state); docs.ifdog.com Mamba tutorial: "离散化"
+ * (ZOH, diagonal A), "Mamba：选择性状态空间模型" (softplus, input-dependent B/C/Delta), "Mamba 架构" (SiLU gate)):
+ *
+ *   for every batch b and channel d independently, with a diagonal state h[0..N-1]:
+ *     Delta_t = softplus(dt[b,d,t] + dt_bias[d])      (or dt + dt_bias when dt_softplus == 0)
+ *     h[n]   <- exp(Delta_t * A[d,n]) * h[n] + Bbar_t[n] * x[b,d,t]
+ *               Bbar_t[n] = Delta_t * B[b,n,t]                         (SSM_DISC_EULER_B, default)
+ *               Bbar_t[n] = expm1(Delta_t*A[d,n]) / A[d,n] * B[b,n,t]  (SSM_DISC_ZOH; A == 0 uses Delta_t * B)
+ *     y[b,d,t] = (sum_n C[b,n,t] * h[n] + Dskip[d] * x[b,d,t]) * silu(z[b,d,t]),  silu(v) = v * sigmoid(v)
+ *   h starts at h0[b,d,:] (zeros when h0 == NULL) and its last value is written to h_final.
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE memory owned by the caller.  The library allocates nothing; the forward scan may
+ *     need a caller-provided workspace (query its size first).
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default stream).  Buffers must stay
+ *     alive until the stream has executed the call.  Nothing is synchronised implicitly.
+ *   - Layouts are row-major with the sequence index innermost:  x, dt, z, y: [batch][dim][seqlen];
+ *     B, C: [batch][dstate][seqlen];  A: [dim][dstate];  dt_bias, Dskip: [dim];  h0, h_final, state: [batch][dim][dstate].
+ *     Decode tensors drop the seqlen axis: x, dt, z, y: [batch][dim];  B, C: [batch][dstate].
+ *   - x, dt, B, C, z use params.io_dtype (fp32, or bf16 stored as its 16-bit pattern); y uses params.y_dtype;
+ *     A, dt_bias, Dskip, h0, h_final, state and the arithmetic are fp32.  bf16 outputs are rounded to nearest-even.
+ *   - Argument errors are reported BEFORE anything is launched: a non-OK status means no kernel ran and no output was
+ *     touched.  Launch failures report SSM_ERR_HIP.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, as with any asynchronous HIP work.  Non-finite inputs are not checked; they propagate.
+ *   - y must not overlap any input.  h_final may alias h0.  The decode state is updated in place.
+ *   - Results are deterministic: the same inputs and parameters give bit-identical outputs on every run.
+ *   - Every function is reentrant; ssm_last_error() is thread-local.
+ */
+#ifndef SSM57_SSM_SCAN_H
+#define SSM57_SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM57_ABI_VERSION 1
+#define SSM57_MAX_DSTATE 16
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,         /* a required pointer is NULL */
+  SSM_ERR_SHAPE = 2,        /* batch/dim/seqlen < 1, dstate outside [1, 16], sizes that overflow the grid */
+  SSM_ERR_DTYPE = 3,        /* unknown io_dtype / y_dtype */
+  SSM_ERR_UNSUPPORTED = 4,  /* unknown disc or dt_softplus value, negative segments */
+  SSM_ERR_ALIGN = 5,        /* a pointer not aligned to its element size */
+  SSM_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ssm_scan_fwd_workspace_bytes() */
+  SSM_ERR_HIP = 7           /* the HIP runtime refused a launch */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+  SSM_DISC_EULER_B = 0, /* Abar = exp(Delta A), Bbar = Delta B (the tutorial's simplified selective SSM) */
+  SSM_DISC_ZOH = 1      /* Abar = exp(Delta A), Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B  (paper eq. (4)) */
+} ssm_disc;
+
+typedef struct {
+  int64_t batch;       /* b >= 1 */
+  int64_t dim;         /* D >= 1 channels (d_inner) */
+  int64_t seqlen;      /* L >= 1 (ignored by ssm_state_update) */
+  int64_t dstate;      /* N, 1 <= N <= 16 */
+  int32_t io_dtype;    /* ssm_dtype of x, dt, B, C, z */
+  int32_t y_dtype;     /* ssm_dtype of y */
+  int32_t disc;        /* ssm_disc */
+  int32_t dt_softplus; /* 1: Delta = softplus(dt + dt_bias); 0: Delta = dt + dt_bias */
+  int32_t segments;    /* 0: the library picks the number of L-segments scanned in parallel; k > 0 forces k
+                          (clamped to the number of 64-step chunks); results agree within rounding either way */
+  int32_t reserved;    /* must be 0 */
+} ssm_scan_params;
+
+/* Bytes of device workspace ssm_scan_fwd needs for these parameters (0 when none).  Pure host function. */
+size_t ssm_scan_fwd_workspace_bytes(const ssm_scan_params* p);
+
+/*
+ * Full-sequence forward scan (steps: softplus Delta, discretisation, recurrence, C-contraction, D skip, SiLU gate).
+ *   x, dt [batch][dim][seqlen] io_dtype;  dt_bias [dim] fp32 or NULL (= 0);  A [dim][dstate] fp32 (the diagonal of A;
+ *   the method expects negative reals, not checked);  B, C [batch][dstate][seqlen] io_dtype;  Dskip [dim] fp32 or NULL
+ *   (= no skip);  z [batch][dim][seqlen] io_dtype or NULL (= no gate);  h0 [batch][dim][dstate] fp32 or NULL (= 0);
+ *   y [batch][dim][seqlen] y_dtype (written);  h_final [batch][dim][dstate] fp32 or NULL (written; may alias h0);
+ *   workspace: device buffer of at least ssm_scan_fwd_workspace_bytes(p) bytes, 4-byte aligned (NULL if 0 needed);
+ *   stream: hipStream_t or NULL.
+ */
+ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
+                        const void* B, const void* C, const float* Dskip, const void* z, const float* h0, void* y,
+                        float* h_final, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Single-token recurrent decode step (constant time and state per token; paper section 1 (ii) and section 2
+ * "recurrent mode (2) for autoregressive inference").  Same arithmetic as one step of ssm_scan_fwd.
+ *   state [batch][dim][dstate] fp32, read and overwritten in place;  x, dt, z, y [batch][dim];  B, C [batch][dstate];
+ *   dt_bias, A, Dskip as above.  p->seqlen and p->segments are ignored.
+ */
+ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* x, const void* dt,
+                            const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
+                            const void* z, void* y, void* stream);
+
+/* Static description of a status code. */
+const char* ssm_status_str(ssm_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* ssm_last_error(void);
+
+/* SSM57_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+/* Number of L-segments ssm_scan_fwd would use for these parameters (>= 1), or 0 for invalid parameters. */
+int ssm_scan_fwd_plan_segments(const ssm_scan_params* p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM57_SSM_SCAN_H */

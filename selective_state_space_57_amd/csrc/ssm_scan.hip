@@ -1,0 +1,634 @@
+// MI355X (gfx950) S6 selective scan: HIP kernels and the C ABI declared in include/ssm_scan.h.
+//
+// What is computed: the per-channel diagonal selective SSM of the Mamba paper (arXiv 2312.00752; gitcode.csdn.net
+// translation, sections 2, 3.2, 3.3.2) with the discretisation and gate of the docs.ifdog.com Mamba tutorial
+// ("离散化", "Mamba 架构"); see the header for the formulas.  The paper's A100 kernel (fusion, state kept on chip,
+// parallel scan) is prior art; the design here is chosen for CDNA4's execution model:
+//
+//  * The work is ALU-bound on this chip, not HBM-bound: every (channel, step) needs N = 16 exponentials and ~4N FMAs
+//    for ~8 bytes of HBM traffic, while v_exp_f32 costs about two FMA issue slots.  So the kernel minimises VALU
+//    slots and balances them perfectly over the 1024 SIMDs.
+//  * One lane owns one (channel, n) state value: a 16-lane DPP row holds the 16 states of one channel, a wave four
+//    channels, a 256-thread workgroup sixteen channels.  Every lane runs the recurrence sequentially in time with its
+//    state in a VGPR; parallelism comes from channels x states, which needs no extra arithmetic (a time-parallel scan
+//    costs more VALU than it saves here).
+//  * Per step, Delta and Delta*x are per channel: lane j of the row computes them for step j of a 16-step block, and
+//    the scan reads them with DPP row_newbcast, which folds into the consuming v_mul at no cost.
+//  * B is staged per 64-step chunk in LDS as fp32 (converted once per workgroup, shared by its 16 channels).
+//  * The C-contraction y_t = sum_n C_n(t) h_n(t) is a transposition: each lane writes its 16 states of a block to LDS,
+//    then lane j of the row reads the 16 states of step j together with C(t) and does 16 FMAs, adds D x, applies the
+//    SiLU gate and stores y.  That lane is the same one that loaded x and z of step j, so no other data moves.
+//  * Long sequences with few channels (a million steps on 512 channels) are split into L-segments: a first pass
+//    computes every segment's zero-start end state and sum of Delta, a tiny pass chains them into carry-in states
+//    (exp(A * sum Delta) is the product of the segment's decays), and the main pass rescans each segment from its
+//    carry-in.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <utility>
+
+#include "ssm_scan.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kChanPerWG = 16;  // 16 rows of 16 lanes
+constexpr int kChunk = 64;      // steps per B/C staging chunk
+constexpr int kSub = 16;        // steps per transposition block (= lanes per row)
+constexpr int kBStride = kChunk + 4;   // sB row stride (floats): conflict-free b128 column reads
+constexpr int kCtStride = kSub + 4;    // sCt/sH step stride (floats)
+constexpr int kHRow = kSub * kCtStride + 16;  // sH row stride: rows of one wave land on different banks
+
+// ---------------------------------------------------------------------------------------------------------------
+// element access
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <>
+struct Elem<uint16_t> {  // bf16 stored as its bit pattern
+  static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
+    p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32: round to nearest even
+  }
+};
+
+// ---------------------------------------------------------------------------------------------------------------
+// scalar math (fp32).  exp2/log2/rcp are the hardware transcendental instructions.
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + v) for v in [0, 1]: log(w) * v / (w - 1) with w = fl(1 + v) cancels the rounding of 1 + v (Goldberg,
+// "What every computer scientist should know about floating-point arithmetic", log1p via the correction factor).
+__device__ __forceinline__ float log1p_01(float v) {
+  float w = 1.0f + v;
+  float wm1 = w - 1.0f;
+  float r = hw_log2(w) * kLn2 * (v * hw_rcp(wm1));
+  return wm1 == 0.0f ? v : r;
+}
+
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e^-|u|)   (tau_Delta of paper section 3.2)
+__device__ __forceinline__ float softplus(float u) {
+  float v = hw_exp2(-fabsf(u) * kLog2e);
+  return fmaxf(u, 0.0f) + log1p_01(v);
+}
+
+// silu(z) = z * sigmoid(z)   (gate of the Mamba block)
+__device__ __forceinline__ float silu(float z) { return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e)); }
+
+// expm1(e) given a = exp(e): Taylor polynomial near 0 (|e| < 1/4, truncation < 2e-10 relative), a - 1 elsewhere.
+__device__ __forceinline__ float expm1_from(float e, float a) {
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, e, 1.0f / 720.0f);
+  p = fmaf(p, e, 1.0f / 120.0f);
+  p = fmaf(p, e, 1.0f / 24.0f);
+  p = fmaf(p, e, 1.0f / 6.0f);
+  p = fmaf(p, e, 0.5f);
+  p = fmaf(p, e, 1.0f);
+  p = p * e;
+  return fabsf(e) < 0.25f ? p : a - 1.0f;
+}
+
+// broadcast lane K of each 16-lane row (DPP row_newbcast); folds into the consuming VALU instruction
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf,
+                                                               false));
+}
+
+template <typename F, int... Ks>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
+  (f(std::integral_constant<int, Ks>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct ScanArgs {
+  const void* x;
+  const void* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  const float* h0;
+  void* y;
+  float* h_final;
+  float* ws_h;    // [nseg][batch*dim][N]: segment end states (first pass), then carry-in states
+  float* ws_sum;  // [nseg][batch*dim]: per-segment sum of Delta
+  int64_t batch, dim, L, seg_len;
+  int N, nseg, softplus;
+};
+
+// ---------------------------------------------------------------------------------------------------------------
+// The scan kernel.  AGG = true: first pass of the segmented scan (zero start, no output; writes the end state and
+// the sum of Delta of each segment).  AGG = false: the fused forward scan of one segment (or the whole sequence).
+template <typename TI, typename TY, bool ZOH, bool AGG, bool GATE, bool DSKIP>
+__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
+  __shared__ __align__(16) float sB[kChanPerWG][kBStride];           // B_n(t) of the chunk, [n][t]
+  __shared__ __align__(16) float sCt[AGG ? 1 : kChunk][kCtStride];   // C_n(t) of the chunk, [t][n]
+  __shared__ __align__(16) float sH[AGG ? 1 : kChanPerWG * kHRow];   // states of a 16-step block, per row [t][n]
+
+  const int tid = threadIdx.x;
+  const int n = tid & 15;    // state index of this lane; also the step index it owns within a 16-step block
+  const int row = tid >> 4;  // channel within the workgroup
+  const int64_t d = static_cast<int64_t>(blockIdx.x) * kChanPerWG + row;
+  const int64_t b = blockIdx.y;
+  const int seg = blockIdx.z;
+  const bool chv = d < p.dim;
+  const bool nv = n < p.N;
+  const int64_t ch = b * p.dim + d;
+  const int64_t ts = static_cast<int64_t>(seg) * p.seg_len;
+  const int64_t te = ts + p.seg_len < p.L ? ts + p.seg_len : p.L;
+  const int64_t bdN = p.batch * p.dim;
+
+  const TI* __restrict__ xr = static_cast<const TI*>(p.x) + (chv ? ch * p.L : 0);
+  const TI* __restrict__ dr = static_cast<const TI*>(p.dt) + (chv ? ch * p.L : 0);
+  const TI* __restrict__ zr = GATE ? static_cast<const TI*>(p.z) + (chv ? ch * p.L : 0) : nullptr;
+  TY* __restrict__ yr = AGG ? nullptr : static_cast<TY*>(p.y) + (chv ? ch * p.L : 0);
+  const TI* __restrict__ Bg = static_cast<const TI*>(p.B) + b * p.N * p.L;
+  const TI* __restrict__ Cg = static_cast<const TI*>(p.C) + b * p.N * p.L;
+
+  const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
+  const float Ap = An * kLog2e;                                   // exp(Delta*A) = exp2(Delta*A*log2(e))
+  const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
+  const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
+  const float Dv = (DSKIP && chv) ? p.Dskip[d] : 0.0f;
+
+  float h = 0.0f;
+  if (!AGG && chv && nv) {
+    if (p.nseg > 1)
+      h = p.ws_h[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n];
+    else if (p.h0)
+      h = p.h0[ch * p.N + n];
+  }
+  float dsum = 0.0f;  // AGG: this lane's share of the segment's sum of Delta
+
+  float* const hrow = AGG ? nullptr : &sH[row * kHRow];
+
+  for (int64_t t0 = ts; t0 < te; t0 += kChunk) {
+    // ---- stage B (and C) of steps [t0, t0 + 64) as fp32; thread (nn, q) converts steps 4q..4q+3 of state nn
+    __syncthreads();
+    {
+      const int nn = tid >> 4, q = tid & 15;
+      float bv[4], cv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t t = t0 + 4 * q + k;
+        const bool ok = nn < p.N && t < te;
+        bv[k] = ok ? Elem<TI>::ld(Bg, nn * p.L + t) : 0.0f;
+        cv[k] = (!AGG && ok) ? Elem<TI>::ld(Cg, nn * p.L + t) : 0.0f;
+      }
+      *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      if (!AGG) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sCt[4 * q + k][nn] = cv[k];
+      }
+    }
+    __syncthreads();
+
+    for (int s = 0; s < kChunk / kSub; ++s) {
+      const int64_t tb = t0 + s * kSub;
+      if (tb >= te) break;  // uniform across the workgroup
+      // ---- owned step: t = tb + n of channel d
+      const int64_t t = tb + n;
+      const bool ev = chv && t < te;
+      const float xv = ev ? Elem<TI>::ld(xr, t) : 0.0f;
+      float zv = 0.0f;
+      if (GATE) zv = ev ? Elem<TI>::ld(zr, t) : 0.0f;
+      const float u = ev ? Elem<TI>::ld(dr, t) + bias : 0.0f;
+      float delta = p.softplus ? softplus(u) : u;
+      delta = ev ? delta : 0.0f;  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
+      const float dx = delta * xv;
+      if (AGG) dsum += delta;
+
+      // ---- B_n(tb .. tb+15) from LDS
+      float bq[kSub];
+#pragma unroll
+      for (int i = 0; i < kSub / 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(&sB[n][s * kSub + 4 * i]);
+        bq[4 * i + 0] = v.x;
+        bq[4 * i + 1] = v.y;
+        bq[4 * i + 2] = v.z;
+        bq[4 * i + 3] = v.w;
+      }
+
+      // ---- 16 sequential steps of the recurrence for this lane's state
+      float hv[kSub];
+      static_for<kSub>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const float dk = row_bcast<k>(delta);
+        const float a = hw_exp2(dk * Ap);
+        float bb;
+        if (ZOH) {
+          const float en = dk * An;
+          const float coef = An != 0.0f ? expm1_from(en, a) * rA : dk;
+          bb = coef * bq[k] * row_bcast<k>(xv);
+        } else {
+          bb = row_bcast<k>(dx) * bq[k];
+        }
+        h = fmaf(a, h, bb);
+        hv[k] = h;
+      });
+
+      if (!AGG) {
+        // ---- transpose through LDS: lane j of the row gathers h_n(tb + j) for all n and contracts with C
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) hrow[k * kCtStride + n] = hv[k];
+        wave_lds_sync();
+        float acc = 0.0f;
+        const float* hs = &hrow[n * kCtStride];
+        const float* cs = &sCt[s * kSub + n][0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 hh = *reinterpret_cast<const float4*>(hs + 4 * i);
+          const float4 cc = *reinterpret_cast<const float4*>(cs + 4 * i);
+          acc = fmaf(cc.x, hh.x, acc);
+          acc = fmaf(cc.y, hh.y, acc);
+          acc = fmaf(cc.z, hh.z, acc);
+          acc = fmaf(cc.w, hh.w, acc);
+        }
+        if (DSKIP) acc = fmaf(Dv, xv, acc);
+        if (GATE) acc *= silu(zv);
+        if (ev) Elem<TY>::st(yr, t, acc);
+      }
+    }
+  }
+
+  if (AGG) {
+    if (chv && nv) p.ws_h[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n] = h;
+    // sum of Delta over the row's 16 owners
+    dsum += __shfl_xor(dsum, 8, 16);
+    dsum += __shfl_xor(dsum, 4, 16);
+    dsum += __shfl_xor(dsum, 2, 16);
+    dsum += __shfl_xor(dsum, 1, 16);
+    if (chv && n == 0) p.ws_sum[static_cast<int64_t>(seg) * bdN + ch] = dsum;
+  } else {
+    if (p.h_final && chv && nv && seg == p.nseg - 1) p.h_final[ch * p.N + n] = h;
+  }
+}
+
+// Chains the segment aggregates into carry-in states: h_in[0] = h0, h_in[s+1] = exp(A * sum_s Delta) h_in[s] + e_s,
+// where e_s is segment s's end state from a zero start (the associative combine of the tutorial's parallel scan).
+__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A, const float* __restrict__ h0,
+                                                    float* __restrict__ ws_h, const float* __restrict__ ws_sum,
+                                                    int64_t batch, int64_t dim, int N, int nseg) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t bdN = batch * dim;
+  if (i >= bdN * N) return;
+  const int64_t ch = i / N;
+  const int n = static_cast<int>(i % N);
+  const int64_t d = ch % dim;
+  const float Ap = A[d * N + n] * kLog2e;
+  float run = h0 ? h0[i] : 0.0f;
+  for (int s = 0; s < nseg; ++s) {
+    const int64_t k = static_cast<int64_t>(s) * bdN * N + i;
+    const float e = (s < nseg - 1) ? ws_h[k] : 0.0f;
+    const float sum = (s < nseg - 1) ? ws_sum[static_cast<int64_t>(s) * bdN + ch] : 0.0f;
+    ws_h[k] = run;
+    run = fmaf(hw_exp2(sum * Ap), run, e);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// Decode: one step per (batch, channel).  HBM-bound (the fp32 state is read and written once), so the layout is
+// chosen for coalescing: a quad of lanes owns one channel, each lane four consecutive states (one 16-byte access).
+struct DecodeArgs {
+  float* state;
+  const void* x;
+  const void* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  void* y;
+  int64_t batch, dim;
+  int N, softplus;
+};
+
+template <typename TI, typename TY, bool ZOH, bool VEC>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
+  const int tid = threadIdx.x;
+  const int q = tid & 3;
+  const int64_t d = static_cast<int64_t>(blockIdx.x) * 64 + (tid >> 2);
+  const int64_t b = blockIdx.y;
+  const bool chv = d < p.dim;
+  const int64_t ch = b * p.dim + d;
+  float xv = 0.0f, u = 0.0f, zv = 0.0f;
+  if (chv) {
+    xv = Elem<TI>::ld(static_cast<const TI*>(p.x), ch);
+    u = Elem<TI>::ld(static_cast<const TI*>(p.dt), ch) + (p.dt_bias ? p.dt_bias[d] : 0.0f);
+    if (p.z) zv = Elem<TI>::ld(static_cast<const TI*>(p.z), ch);
+  }
+  const float delta = p.softplus ? softplus(u) : u;
+  const float dx = delta * xv;
+  const TI* Bb = static_cast<const TI*>(p.B) + b * p.N;
+  const TI* Cb = static_cast<const TI*>(p.C) + b * p.N;
+  float hs[4], As[4];
+  if (VEC) {
+    if (chv) {
+      const float4 hv = *reinterpret_cast<const float4*>(p.state + ch * 16 + 4 * q);
+      const float4 av = *reinterpret_cast<const float4*>(p.A + d * 16 + 4 * q);
+      hs[0] = hv.x; hs[1] = hv.y; hs[2] = hv.z; hs[3] = hv.w;
+      As[0] = av.x; As[1] = av.y; As[2] = av.z; As[3] = av.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[i] = As[i] = 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = 4 * q + i;
+      const bool ok = chv && nn < p.N;
+      hs[i] = ok ? p.state[ch * p.N + nn] : 0.0f;
+      As[i] = ok ? p.A[d * p.N + nn] : 0.0f;
+    }
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nn = 4 * q + i;
+    const bool ok = nn < p.N;
+    const float Bn = ok ? Elem<TI>::ld(Bb, nn) : 0.0f;
+    const float Cn = ok ? Elem<TI>::ld(Cb, nn) : 0.0f;
+    const float a = hw_exp2(delta * (As[i] * kLog2e));
+    float bb;
+    if (ZOH) {
+      const float en = delta * As[i];
+      const float coef = As[i] != 0.0f ? expm1_from(en, a) * (1.0f / As[i]) : delta;
+      bb = coef * Bn * xv;
+    } else {
+      bb = dx * Bn;
+    }
+    hs[i] = fmaf(a, hs[i], bb);
+    acc = fmaf(Cn, hs[i], acc);
+  }
+  // sum over the quad (DPP quad_perm)
+  acc += __shfl_xor(acc, 1, 4);
+  acc += __shfl_xor(acc, 2, 4);
+  if (VEC) {
+    if (chv) *reinterpret_cast<float4*>(p.state + ch * 16 + 4 * q) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = 4 * q + i;
+      if (chv && nn < p.N) p.state[ch * p.N + nn] = hs[i];
+    }
+  }
+  if (chv && q == 0) {
+    if (p.Dskip) acc = fmaf(p.Dskip[d], xv, acc);
+    if (p.z) acc *= silu(zv);
+    Elem<TY>::st(static_cast<TY*>(p.y), ch, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// host side: validation, planning, dispatch
+
+thread_local char g_err[512] = "";
+
+ssm_status fail(ssm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+ssm_status check_common(const ssm_scan_params* p, bool need_seqlen) {
+  if (!p) return fail(SSM_ERR_NULL, "params is NULL");
+  if (p->batch < 1 || p->dim < 1 || (need_seqlen && p->seqlen < 1))
+    return fail(SSM_ERR_SHAPE, "batch=%lld dim=%lld seqlen=%lld must be >= 1", (long long)p->batch,
+                (long long)p->dim, (long long)p->seqlen);
+  if (p->dstate < 1 || p->dstate > SSM57_MAX_DSTATE)
+    return fail(SSM_ERR_SHAPE, "dstate=%lld must be in [1, %d]", (long long)p->dstate, SSM57_MAX_DSTATE);
+  if (p->io_dtype != SSM_F32 && p->io_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown io_dtype %d", p->io_dtype);
+  if (p->y_dtype != SSM_F32 && p->y_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown y_dtype %d", p->y_dtype);
+  if (p->disc != SSM_DISC_EULER_B && p->disc != SSM_DISC_ZOH)
+    return fail(SSM_ERR_UNSUPPORTED, "unknown disc %d", p->disc);
+  if (p->dt_softplus != 0 && p->dt_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "dt_softplus must be 0 or 1 (got %d)", p->dt_softplus);
+  if (p->segments < 0) return fail(SSM_ERR_UNSUPPORTED, "segments must be >= 0 (got %d)", p->segments);
+  if (p->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved must be 0");
+  // index arithmetic is 64-bit; keep element counts well inside it and the grid inside HIP's limits
+  const double elems = static_cast<double>(p->batch) * static_cast<double>(p->dim) *
+                       static_cast<double>(need_seqlen ? p->seqlen : 1) * 1.0;
+  if (elems > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
+  if (p->batch > 65535) return fail(SSM_ERR_SHAPE, "batch=%lld exceeds 65535", (long long)p->batch);
+  if ((p->dim + 15) / 16 > 0x7fffffffLL) return fail(SSM_ERR_SHAPE, "dim too large");
+  return SSM_OK;
+}
+
+struct Plan {
+  int nseg;
+  int64_t seg_len;
+  size_t ws_bytes;
+};
+
+Plan make_plan(const ssm_scan_params* p) {
+  Plan pl{1, p->seqlen, 0};
+  const int64_t chunks = (p->seqlen + kChunk - 1) / kChunk;
+  int64_t nseg = 1;
+  if (p->segments > 0) {
+    nseg = p->segments;
+  } else {
+    // fill the 1024 SIMDs: one wave per 4 channels; aim for >= 4096 waves, but keep segments >= 1024 steps
+    const int64_t waves = ((p->dim + 15) / 16) * p->batch * 4;
+    if (waves < 2048) {
+      nseg = (4096 + waves - 1) / waves;
+      const int64_t maxseg = (p->seqlen + 1023) / 1024;
+      if (nseg > maxseg) nseg = maxseg;
+    }
+  }
+  if (nseg > chunks) nseg = chunks;
+  if (nseg > 65535) nseg = 65535;
+  if (nseg < 1) nseg = 1;
+  const int64_t seg_chunks = (chunks + nseg - 1) / nseg;
+  pl.seg_len = seg_chunks * kChunk;
+  pl.nseg = static_cast<int>((p->seqlen + pl.seg_len - 1) / pl.seg_len);
+  if (pl.nseg > 1) {
+    const size_t bd = static_cast<size_t>(p->batch) * static_cast<size_t>(p->dim);
+    pl.ws_bytes = static_cast<size_t>(pl.nseg) * bd * (static_cast<size_t>(p->dstate) + 1) * sizeof(float);
+  } else {
+    pl.seg_len = p->seqlen;
+  }
+  return pl;
+}
+
+template <typename TI, typename TY, bool ZOH, bool AGG>
+hipError_t launch_scan_t(const ScanArgs& a, dim3 grid, hipStream_t st, bool gate, bool dskip) {
+  if (gate && dskip) hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, true, true>), grid, dim3(kThreads), 0, st, a);
+  else if (gate) hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, true, false>), grid, dim3(kThreads), 0, st, a);
+  else if (dskip) hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, false, true>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, false, false>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename TI, bool ZOH>
+hipError_t launch_scan_io(const ScanArgs& a, dim3 grid, hipStream_t st, bool agg, int ydt, bool gate, bool dskip) {
+  if (agg) return launch_scan_t<TI, float, ZOH, true>(a, grid, st, false, false);
+  if (ydt == SSM_F32) return launch_scan_t<TI, float, ZOH, false>(a, grid, st, gate, dskip);
+  return launch_scan_t<TI, uint16_t, ZOH, false>(a, grid, st, gate, dskip);
+}
+
+hipError_t launch_scan(const ScanArgs& a, dim3 grid, hipStream_t st, bool agg, const ssm_scan_params* p) {
+  const bool gate = a.z != nullptr, dskip = a.Dskip != nullptr;
+  if (p->io_dtype == SSM_F32) {
+    return p->disc == SSM_DISC_ZOH ? launch_scan_io<float, true>(a, grid, st, agg, p->y_dtype, gate, dskip)
+                                   : launch_scan_io<float, false>(a, grid, st, agg, p->y_dtype, gate, dskip);
+  }
+  return p->disc == SSM_DISC_ZOH ? launch_scan_io<uint16_t, true>(a, grid, st, agg, p->y_dtype, gate, dskip)
+                                 : launch_scan_io<uint16_t, false>(a, grid, st, agg, p->y_dtype, gate, dskip);
+}
+
+template <typename TI, typename TY, bool ZOH>
+hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, hipStream_t st, bool vec) {
+  if (vec) hipLaunchKernelGGL((decode_kernel<TI, TY, ZOH, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((decode_kernel<TI, TY, ZOH, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t launch_decode_io(const DecodeArgs& a, dim3 grid, hipStream_t st, const ssm_scan_params* p, bool vec) {
+  const bool zoh = p->disc == SSM_DISC_ZOH;
+  if (p->y_dtype == SSM_F32)
+    return zoh ? launch_decode_t<TI, float, true>(a, grid, st, vec) : launch_decode_t<TI, float, false>(a, grid, st, vec);
+  return zoh ? launch_decode_t<TI, uint16_t, true>(a, grid, st, vec)
+             : launch_decode_t<TI, uint16_t, false>(a, grid, st, vec);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_fwd_workspace_bytes(const ssm_scan_params* p) {
+  if (check_common(p, true) != SSM_OK) return 0;
+  return make_plan(p).ws_bytes;
+}
+
+int ssm_scan_fwd_plan_segments(const ssm_scan_params* p) {
+  if (check_common(p, true) != SSM_OK) return 0;
+  return make_plan(p).nseg;
+}
+
+ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
+                        const void* B, const void* C, const float* Dskip, const void* z, const float* h0, void* y,
+                        float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  ssm_status s = check_common(p, true);
+  if (s != SSM_OK) return s;
+  if (!x || !dt || !A || !B || !C || !y) return fail(SSM_ERR_NULL, "x, dt, A, B, C and y are required");
+  const size_t io = p->io_dtype == SSM_F32 ? 4 : 2, ys = p->y_dtype == SSM_F32 ? 4 : 2;
+  if (!aligned(x, io) || !aligned(dt, io) || !aligned(B, io) || !aligned(C, io) || (z && !aligned(z, io)) ||
+      !aligned(y, ys) || !aligned(A, 4) || (dt_bias && !aligned(dt_bias, 4)) || (Dskip && !aligned(Dskip, 4)) ||
+      (h0 && !aligned(h0, 4)) || (h_final && !aligned(h_final, 4)))
+    return fail(SSM_ERR_ALIGN, "a pointer is not aligned to its element size");
+  const Plan pl = make_plan(p);
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 4)) return fail(SSM_ERR_ALIGN, "workspace must be 4-byte aligned");
+  }
+  ScanArgs a{};
+  a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z; a.h0 = h0;
+  a.y = y; a.h_final = h_final;
+  a.batch = p->batch; a.dim = p->dim; a.L = p->seqlen; a.seg_len = pl.seg_len;
+  a.N = static_cast<int>(p->dstate); a.nseg = pl.nseg; a.softplus = p->dt_softplus;
+  const size_t bd = static_cast<size_t>(p->batch) * static_cast<size_t>(p->dim);
+  if (pl.nseg > 1) {
+    a.ws_h = static_cast<float*>(workspace);
+    a.ws_sum = a.ws_h + static_cast<size_t>(pl.nseg) * bd * static_cast<size_t>(p->dstate);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned gx = static_cast<unsigned>((p->dim + kChanPerWG - 1) / kChanPerWG);
+  hipError_t e = hipSuccess;
+  if (pl.nseg > 1) {
+    e = launch_scan(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg - 1)), st, true, p);
+    if (e == hipSuccess) {
+      const int64_t tot = static_cast<int64_t>(bd) * p->dstate;
+      hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((tot + 255) / 256)), dim3(256), 0, st, A, h0,
+                         a.ws_h, a.ws_sum, p->batch, p->dim, a.N, pl.nseg);
+      e = hipGetLastError();
+    }
+  }
+  if (e == hipSuccess)
+    e = launch_scan(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg)), st, false, p);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SSM_OK;
+}
+
+ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* x, const void* dt,
+                            const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
+                            const void* z, void* y, void* stream) {
+  g_err[0] = 0;
+  ssm_status s = check_common(p, false);
+  if (s != SSM_OK) return s;
+  if (!state || !x || !dt || !A || !B || !C || !y)
+    return fail(SSM_ERR_NULL, "state, x, dt, A, B, C and y are required");
+  const size_t io = p->io_dtype == SSM_F32 ? 4 : 2, ys = p->y_dtype == SSM_F32 ? 4 : 2;
+  if (!aligned(x, io) || !aligned(dt, io) || !aligned(B, io) || !aligned(C, io) || (z && !aligned(z, io)) ||
+      !aligned(y, ys) || !aligned(A, 4) || !aligned(state, 4) || (dt_bias && !aligned(dt_bias, 4)) ||
+      (Dskip && !aligned(Dskip, 4)))
+    return fail(SSM_ERR_ALIGN, "a pointer is not aligned to its element size");
+  DecodeArgs a{};
+  a.state = state; a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z;
+  a.y = y; a.batch = p->batch; a.dim = p->dim; a.N = static_cast<int>(p->dstate); a.softplus = p->dt_softplus;
+  const bool vec = p->dstate == 16 && aligned(state, 16) && aligned(A, 16);
+  const dim3 grid(static_cast<unsigned>((p->dim + 63) / 64), static_cast<unsigned>(p->batch));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = p->io_dtype == SSM_F32 ? launch_decode_io<float>(a, grid, st, p, vec)
+                                              : launch_decode_io<uint16_t>(a, grid, st, p, vec);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SSM_OK;
+}
+
+const char* ssm_status_str(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid shape";
+    case SSM_ERR_DTYPE: return "invalid dtype";
+    case SSM_ERR_UNSUPPORTED: return "unsupported parameter";
+    case SSM_ERR_ALIGN: return "misaligned pointer";
+    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ssm_last_error(void) { return g_err; }
+
+int ssm_abi_version(void) { return SSM57_ABI_VERSION; }
+
+}  // extern "C"

@@ -19,7 +19,10 @@ Recipe (also written out in the design doc):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
+
 import numpy as np
 
 CHUNK = 1 << 24
@@ -66,28 +69,60 @@ def _rng(cfg: int, step: int, k: int, i: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(cfg, step, k, i)))
 
 
+def _chunks(n):
+    for i, s in enumerate(range(0, n, CHUNK)):
+        yield i, s, min(n, s + CHUNK)
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _fill(n, fn):
+    """Run fn(i, s, e) for every chunk; chunks are seeded independently, so the order does not matter."""
+    ch = list(_chunks(n))
+    if len(ch) <= 1:
+        for c in ch:
+            fn(*c)
+        return
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(lambda c: fn(*c), ch))
+
+
 def _normal(cfg, step, k, n) -> np.ndarray:
     out = np.empty(n, np.float32)
-    for i, s in enumerate(range(0, n, CHUNK)):
-        e = min(n, s + CHUNK)
+
+    def f(i, s, e):
         out[s:e] = _rng(cfg, step, k, i).standard_normal(e - s, dtype=np.float32)
+    _fill(n, f)
     return out
+
+
+def _loguniform_chunk(cfg, step, k, i, m, lo, hi) -> np.ndarray:
+    v = _rng(cfg, step, k, i).uniform(np.log(lo), np.log(hi), m)
+    np.exp(v, out=v)
+    return v
 
 
 def _loguniform(cfg, step, k, n, lo, hi) -> np.ndarray:
     out = np.empty(n, np.float64)
-    llo, lhi = np.log(lo), np.log(hi)
-    for i, s in enumerate(range(0, n, CHUNK)):
-        e = min(n, s + CHUNK)
-        out[s:e] = np.exp(_rng(cfg, step, k, i).uniform(llo, lhi, e - s))
+    for i, s, e in _chunks(n):
+        out[s:e] = _loguniform_chunk(cfg, step, k, i, e - s, lo, hi)
     return out
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest-even), returned as uint16 bit patterns.  Finite inputs only."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -115,6 +150,19 @@ def _softplus_inv(v: np.ndarray) -> np.ndarray:
     return np.log(np.expm1(v))
 
 
+def _storage_empty(n, io):
+    return np.empty(n, np.uint16 if io == BF16 else np.float32)
+
+
+def _normal_storage(cfg, step, k, n, io) -> np.ndarray:
+    out = _storage_empty(n, io)
+
+    def f(i, s, e):
+        out[s:e] = to_storage(_rng(cfg, step, k, i).standard_normal(e - s, dtype=np.float32), io)
+    _fill(n, f)
+    return out
+
+
 def scan_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
     """Inputs for ssm_scan_fwd (or one decode step when w.decode_steps > 0, with seqlen = 1 squeezed away).
 
@@ -124,9 +172,8 @@ def scan_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
     b, D, N = w.batch, w.dim, w.dstate
     L = 1 if w.decode_steps else w.seqlen
     c = w.cfg_id
+    io = w.io
     nx = b * D * L
-    x = _normal(c, step, 0, nx)
-    delta = _loguniform(c, step, 1, nx, w.delta_lo, w.delta_hi)
     # the bias is a per-channel parameter: drawn once (decode step 0) and reused by every step
     bias = _softplus_inv(_loguniform(c, 0, 2, D, w.delta_lo, w.delta_hi)).astype(np.float32)
     base = -(np.arange(N, dtype=np.float64) + 1.0)
@@ -136,23 +183,36 @@ def scan_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
     else:
         A = np.broadcast_to(base, (D, N)).copy()
     A = A.astype(np.float32)
-    Bm = _normal(c, step, 4, b * N * L)
-    Cm = _normal(c, step, 5, b * N * L)
+    x = _normal_storage(c, step, 0, nx, io)
+    dt = _storage_empty(nx, io)
+    bias64 = bias.astype(np.float64)
+
+    def fdt(i, s, e):
+        v = _loguniform_chunk(c, step, 1, i, e - s, w.delta_lo, w.delta_hi)   # Delta*
+        np.expm1(v, out=v)                                                   # softplus^-1(Delta*) ...
+        np.log(v, out=v)
+        if L >= 64:                                                          # ... minus the channel's bias
+            for r in range(s // L, (e - 1) // L + 1):
+                v[max(s, r * L) - s:min(e, (r + 1) * L) - s] -= bias64[r % D]
+        else:
+            v -= bias64[(np.arange(s, e, dtype=np.int64) // L) % D]
+        dt[s:e] = to_storage(v, io)
+    _fill(nx, fdt)
+    Bm = _normal_storage(c, step, 4, b * N * L, io)
+    Cm = _normal_storage(c, step, 5, b * N * L, io)
     Dskip = _normal(c, 0, 6, D) if w.dskip else None
-    z = _normal(c, step, 7, nx) if w.gate else None
-    logit = (_softplus_inv(delta).reshape(b, D, L) - bias.astype(np.float64)[None, :, None]).reshape(-1)
-    io = w.io
+    z = _normal_storage(c, step, 7, nx, io) if w.gate else None
     shp = (b, D) if w.decode_steps else (b, D, L)
     bshp = (b, N) if w.decode_steps else (b, N, L)
     out = {
-        "x": to_storage(x, io).reshape(shp),
-        "dt": to_storage(logit, io).reshape(shp),
+        "x": x.reshape(shp),
+        "dt": dt.reshape(shp),
         "dt_bias": bias,
         "A": A,
-        "B": to_storage(Bm, io).reshape(bshp),
-        "C": to_storage(Cm, io).reshape(bshp),
+        "B": Bm.reshape(bshp),
+        "C": Cm.reshape(bshp),
         "Dskip": None if Dskip is None else Dskip.astype(np.float32),
-        "z": None if z is None else to_storage(z, io).reshape(shp),
+        "z": None if z is None else z.reshape(shp),
         "h0": None,
     }
     if with_h0:

@@ -1,0 +1,133 @@
+"""CPU tests of the C ABI: the library loads, exports every function include/ssm_scan.h declares, and rejects bad
+arguments before launching anything (these calls never reach the HIP runtime, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_57_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail("libssm57.so is not built; run __graft_entry__.build() first")
+    return _abi.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ssm_abi_version() == 1
+    for code in range(8):
+        assert lib.ssm_status_str(code).decode()
+    assert lib.ssm_status_str(99).decode() == "unknown status"
+
+
+def P(**kw):
+    base = dict(batch=2, dim=33, seqlen=100, dstate=16, io_dtype=_abi.SSM_BF16)
+    base.update(kw)
+    return _abi.make_params(**base)
+
+
+FAKE = 0x10000  # a non-NULL, 256-byte aligned address; never dereferenced because validation fails first
+
+
+def call_scan(p, **ptrs):
+    names = ["x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "h0", "y", "h_final", "ws"]
+    v = {k: FAKE for k in ["x", "dt", "A", "B", "C", "y"]}
+    v.update(ptrs)
+    args = [v.get(k, 0) for k in names]
+    return _abi.scan_fwd_raw(p, *args[:11], args[11], ptrs.get("ws_bytes", 0), 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(dim=0), 2), (dict(seqlen=0), 2), (dict(dstate=0), 2), (dict(dstate=17), 2),
+    (dict(batch=70000), 2), (dict(io_dtype=5), 3), (dict(y_dtype=9), 3), (dict(disc=2), 4), (dict(softplus=2), 4),
+    (dict(segments=-1), 4),
+])
+def test_param_errors(lib, kw, code):
+    p = P(**{k: v for k, v in kw.items() if k != "softplus"})
+    if "softplus" in kw:
+        p.dt_softplus = kw["softplus"]
+    assert call_scan(p) == code
+    assert lib.ssm_last_error().decode()
+
+
+def test_reserved_must_be_zero(lib):
+    p = P()
+    p.reserved = 1
+    assert call_scan(p) == 4
+
+
+@pytest.mark.parametrize("missing", ["x", "dt", "A", "B", "C", "y"])
+def test_null_required(lib, missing):
+    assert call_scan(P(), **{missing: 0}) == 1
+
+
+def test_misaligned(lib):
+    assert call_scan(P(), x=FAKE + 1) == 5                       # bf16 needs 2-byte alignment
+    assert call_scan(P(io_dtype=_abi.SSM_F32), x=FAKE + 2) == 5  # fp32 needs 4
+    assert call_scan(P(), A=FAKE + 2) == 5
+    assert call_scan(P(), h_final=FAKE + 1) == 5
+
+
+def test_null_params(lib):
+    assert lib.ssm_scan_fwd(None, *([None] * 11), None, 0, None) == 1
+    assert lib.ssm_state_update(None, *([None] * 11)) == 1
+
+
+def test_workspace_query_and_errors(lib):
+    p = P(batch=1, dim=512, seqlen=1 << 20)          # few channels, long sequence: segmented
+    nseg = _abi.plan_segments(p)
+    assert nseg > 1
+    need = _abi.workspace_bytes(p)
+    assert need == nseg * 512 * (16 + 1) * 4
+    assert call_scan(p) == 6                              # no workspace
+    assert call_scan(p, ws=FAKE, ws_bytes=need - 1) == 6  # too small
+    assert call_scan(p, ws=FAKE + 2, ws_bytes=need) == 5  # misaligned workspace
+    q = P(batch=4, dim=5120, seqlen=4096)                 # enough channels: one pass, no workspace
+    assert _abi.plan_segments(q) == 1 and _abi.workspace_bytes(q) == 0
+    q.segments = 7
+    assert _abi.plan_segments(q) == 7 and _abi.workspace_bytes(q) == 7 * 4 * 5120 * 17 * 4
+    q.segments = 10 ** 6                                   # clamped to the number of 64-step chunks
+    assert _abi.plan_segments(q) == 4096 // 64
+    assert _abi.workspace_bytes(P(dim=0)) == 0 and _abi.plan_segments(P(dim=0)) == 0
+
+
+def test_state_update_errors(lib):
+    p = P(seqlen=0)  # seqlen is ignored by decode
+    args = [FAKE] * 6 + [0, 0, FAKE, 0, 0]  # state, x, dt, (bias 0)...
+    # order: state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream
+    ok = dict(state=FAKE, x=FAKE, dt=FAKE, dt_bias=0, A=FAKE, B=FAKE, C=FAKE, Dskip=0, z=0, y=FAKE)
+    for k in ["state", "x", "dt", "A", "B", "C", "y"]:
+        a = dict(ok)
+        a[k] = 0
+        assert _abi.state_update_raw(P(dstate=16), **a, stream=0) == 1, k
+    a = dict(ok)
+    a["state"] = FAKE + 2
+    assert _abi.state_update_raw(P(), **a, stream=0) == 5
+    assert _abi.state_update_raw(P(dstate=20), **ok, stream=0) == 2
+    del args
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _abi.lib()
