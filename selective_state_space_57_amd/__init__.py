@@ -25,6 +25,29 @@ def _addr(t):
     return 0 if t is None else t.data_ptr()
 
 
+def _expect(name, t, shape, dtype=None, device=None, optional=True):
+    if t is None:
+        if not optional:
+            raise ValueError("%s is required" % name)
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s: expected dtype %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _out_dtype(y, y_dtype, default):
+    if y is not None:
+        if y_dtype is not None and y_dtype != y.dtype:
+            raise TypeError("y_dtype %s does not match the given y (%s)" % (y_dtype, y.dtype))
+        return y.dtype
+    return default if y_dtype is None else y_dtype
+
+
 def _stream_handle(stream, device):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -43,12 +66,21 @@ def scan_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=Non
     b, D, L = x.shape
     N = A.shape[1]
     io = io_code(x.dtype)
-    ydt = x.dtype if y_dtype is None else y_dtype
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    _expect("x", x, (b, D, L), x.dtype, dev, optional=False)
+    _expect("dt", dt, (b, D, L), x.dtype, dev, optional=False)
+    _expect("z", z, (b, D, L), x.dtype, dev)
+    _expect("B", B, (b, N, L), x.dtype, dev, optional=False)
+    _expect("C", C, (b, N, L), x.dtype, dev, optional=False)
+    _expect("A", A, (D, N), f32, dev, optional=False)
+    _expect("dt_bias", dt_bias, (D,), f32, dev)
+    _expect("Dskip", Dskip, (D,), f32, dev)
+    _expect("h0", h0, (b, D, N), f32, dev)
+    _expect("y", y, (b, D, L), ydt, dev)
+    _expect("h_final", h_final, (b, D, N), f32, dev)
     p = make_params(b, D, L, N, io, io_code(ydt), disc, softplus, segments)
-    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("z", z), ("A", A), ("dt_bias", dt_bias),
-                    ("Dskip", Dskip), ("h0", h0)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
     if y is None:
         y = torch.empty((b, D, L), dtype=ydt, device=x.device)
     if h_final is None and return_final_state:
@@ -70,7 +102,19 @@ def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=N
     import torch
     b, D, N = state.shape
     io = io_code(x.dtype)
-    ydt = x.dtype if y_dtype is None else y_dtype
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    _expect("state", state, (b, D, N), f32, dev, optional=False)
+    _expect("x", x, (b, D), x.dtype, dev, optional=False)
+    _expect("dt", dt, (b, D), x.dtype, dev, optional=False)
+    _expect("z", z, (b, D), x.dtype, dev)
+    _expect("B", B, (b, N), x.dtype, dev, optional=False)
+    _expect("C", C, (b, N), x.dtype, dev, optional=False)
+    _expect("A", A, (D, N), f32, dev, optional=False)
+    _expect("dt_bias", dt_bias, (D,), f32, dev)
+    _expect("Dskip", Dskip, (D,), f32, dev)
+    _expect("y", y, (b, D), ydt, dev)
     p = make_params(b, D, 1, N, io, io_code(ydt), disc, softplus, 0)
     if y is None:
         y = torch.empty((b, D), dtype=ydt, device=x.device)

@@ -44,6 +44,8 @@ constexpr int kSub = 16;        // steps per transposition block (= lanes per ro
 constexpr int kBStride = kChunk + 4;   // sB row stride (floats): conflict-free b128 column reads
 constexpr int kCtStride = kSub + 4;    // sCt/sH step stride (floats)
 constexpr int kHRow = kSub * kCtStride + 16;  // sH row stride: rows of one wave land on different banks
+// 16 rows x L x 4 bytes must stay below 2^31 (buffer offsets; larger offsets address the drop region)
+constexpr int64_t kMaxSeqlen = int64_t(1) << 25;
 
 // ---------------------------------------------------------------------------------------------------------------
 // element access
@@ -52,16 +54,61 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
+  using Raw = float;
+  static __device__ __forceinline__ float cvt(Raw r) { return r; }
   static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
   static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <>
 struct Elem<uint16_t> {  // bf16 stored as its bit pattern
+  using Raw = uint16_t;
+  static __device__ __forceinline__ float cvt(Raw r) { return __uint_as_float(static_cast<uint32_t>(r) << 16); }
   static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
   }
   static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
     p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32: round to nearest even
+  }
+};
+
+// ---------------------------------------------------------------------------------------------------------------
+// buffer (resource-descriptor) access: one descriptor per workgroup and tensor, 32-bit byte offsets per lane.  A read
+// past num_records returns 0 and a write past it is dropped, so partial tiles need no clamping and cannot fault.
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords: the gfx9-family descriptor format
+constexpr uint32_t kDropOffset = 0x80000000u;  // >= every num_records used below: the access is out of range
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, int64_t elems) {
+  int64_t bytes = elems * static_cast<int64_t>(sizeof(T));
+  bytes = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           static_cast<int>(kRsrcWord3));
+}
+
+template <typename T>
+struct Buf;
+template <>
+struct Buf<float> {
+  using Raw = float;
+  static __device__ __forceinline__ Raw ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+  }
+  static __device__ __forceinline__ float cvt(Raw v) { return v; }
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, static_cast<int>(off), 0, 0);
+  }
+};
+template <>
+struct Buf<uint16_t> {
+  using Raw = uint16_t;
+  static __device__ __forceinline__ Raw ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0));
+  }
+  static __device__ __forceinline__ float cvt(Raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, static_cast<__bf16>(v)), r, static_cast<int>(off),
+                                          0, 0);
   }
 };
 
@@ -146,6 +193,10 @@ struct ScanArgs {
 // ---------------------------------------------------------------------------------------------------------------
 // The scan kernel.  AGG = true: first pass of the segmented scan (zero start, no output; writes the end state and
 // the sum of Delta of each segment).  AGG = false: the fused forward scan of one segment (or the whole sequence).
+//
+// Per 64-step chunk a lane owns four steps of its channel (t0 + 16 s + n, s = 0..3) for loading x, dt, z, computing
+// Delta and Delta*x, contracting with C and storing y, plus four B and four C values it stages into LDS.  All of
+// these global loads are issued one chunk ahead, so their latency hides behind a whole chunk of arithmetic.
 template <typename TI, typename TY, bool ZOH, bool AGG, bool GATE, bool DSKIP>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
   __shared__ __align__(16) float sB[kChanPerWG][kBStride];           // B_n(t) of the chunk, [n][t]
@@ -161,16 +212,28 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
   const bool chv = d < p.dim;
   const bool nv = n < p.N;
   const int64_t ch = b * p.dim + d;
-  const int64_t ts = static_cast<int64_t>(seg) * p.seg_len;
-  const int64_t te = ts + p.seg_len < p.L ? ts + p.seg_len : p.L;
+  const int L = static_cast<int>(p.L);  // the host guarantees L < 2^31 - 64
+  const int ts = seg * static_cast<int>(p.seg_len);
+  const int te = ts + static_cast<int>(p.seg_len) < L ? ts + static_cast<int>(p.seg_len) : L;
   const int64_t bdN = p.batch * p.dim;
 
-  const TI* __restrict__ xr = static_cast<const TI*>(p.x) + (chv ? ch * p.L : 0);
-  const TI* __restrict__ dr = static_cast<const TI*>(p.dt) + (chv ? ch * p.L : 0);
-  const TI* __restrict__ zr = GATE ? static_cast<const TI*>(p.z) + (chv ? ch * p.L : 0) : nullptr;
-  TY* __restrict__ yr = AGG ? nullptr : static_cast<TY*>(p.y) + (chv ? ch * p.L : 0);
-  const TI* __restrict__ Bg = static_cast<const TI*>(p.B) + b * p.N * p.L;
-  const TI* __restrict__ Cg = static_cast<const TI*>(p.C) + b * p.N * p.L;
+  // descriptors start at the workgroup's first channel row (x, dt, z, y) and at the batch's B / C rows
+  const int64_t row0 = b * p.dim + static_cast<int64_t>(blockIdx.x) * kChanPerWG;
+  const int64_t rows_left = p.batch * p.dim - row0;
+  const auto rx_ = make_rsrc(static_cast<const TI*>(p.x) + row0 * p.L, rows_left * p.L);
+  const auto rd_ = make_rsrc(static_cast<const TI*>(p.dt) + row0 * p.L, rows_left * p.L);
+  const auto rz_ = make_rsrc(GATE ? static_cast<const TI*>(p.z) + row0 * p.L : static_cast<const TI*>(p.x),
+                             GATE ? rows_left * p.L : 0);
+  const auto ry_ = make_rsrc(AGG ? static_cast<const TY*>(nullptr) : static_cast<const TY*>(p.y) + row0 * p.L,
+                             AGG ? 0 : rows_left * p.L);
+  const auto rb_ = make_rsrc(static_cast<const TI*>(p.B) + b * p.N * p.L, static_cast<int64_t>(p.N) * p.L);
+  const auto rc_ = make_rsrc(static_cast<const TI*>(p.C) + b * p.N * p.L, static_cast<int64_t>(p.N) * p.L);
+  const int nn = tid >> 4, q = tid & 15;  // staging role: B/C of state nn at steps 4q .. 4q+3 of the chunk
+  const bool nnv = nn < p.N;
+  constexpr uint32_t SI = sizeof(TI), SY = sizeof(TY);
+  const uint32_t lane_xo = (static_cast<uint32_t>(row) * static_cast<uint32_t>(L) + n) * SI;  // + t0 * SI
+  const uint32_t lane_yo = (static_cast<uint32_t>(row) * static_cast<uint32_t>(L) + n) * SY;
+  const uint32_t lane_bo = (static_cast<uint32_t>(nn) * static_cast<uint32_t>(L) + 4 * q) * SI;
 
   const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
   const float Ap = An * kLog2e;                                   // exp(Delta*A) = exp2(Delta*A*log2(e))
@@ -186,42 +249,66 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
       h = p.h0[ch * p.N + n];
   }
   float dsum = 0.0f;  // AGG: this lane's share of the segment's sum of Delta
-
   float* const hrow = AGG ? nullptr : &sH[row * kHRow];
 
-  for (int64_t t0 = ts; t0 < te; t0 += kChunk) {
-    // ---- stage B (and C) of steps [t0, t0 + 64) as fp32; thread (nn, q) converts steps 4q..4q+3 of state nn
-    __syncthreads();
-    {
-      const int nn = tid >> 4, q = tid & 15;
-      float bv[4], cv[4];
+  // raw (unconverted) prefetch registers for one chunk.  Reads past the tensors return 0; reads past the segment
+  // or the row are masked off below.
+  using Raw = typename Buf<TI>::Raw;
+  Raw rx[4], rd[4], rz[4], rb[4], rc[4];
+  auto fetch = [&](int t0) {
+    const uint32_t xo = lane_xo + static_cast<uint32_t>(t0) * SI;
+    const uint32_t bo = lane_bo + static_cast<uint32_t>(t0) * SI;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t t = t0 + 4 * q + k;
-        const bool ok = nn < p.N && t < te;
-        bv[k] = ok ? Elem<TI>::ld(Bg, nn * p.L + t) : 0.0f;
-        cv[k] = (!AGG && ok) ? Elem<TI>::ld(Cg, nn * p.L + t) : 0.0f;
-      }
-      *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
-      if (!AGG) {
+    for (int s = 0; s < 4; ++s) {
+      rx[s] = Buf<TI>::ld(rx_, xo + s * kSub * SI);
+      rd[s] = Buf<TI>::ld(rd_, xo + s * kSub * SI);
+      if (GATE) rz[s] = Buf<TI>::ld(rz_, xo + s * kSub * SI);
+    }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sCt[4 * q + k][nn] = cv[k];
-      }
+    for (int k = 0; k < 4; ++k) {
+      rb[k] = Buf<TI>::ld(rb_, bo + k * SI);
+      if (!AGG) rc[k] = Buf<TI>::ld(rc_, bo + k * SI);
+    }
+  };
+  // zero a value unless `ok` (bitwise, so that whatever was read at a clamped index cannot leak in)
+  auto keep = [](bool ok, float v) { return __int_as_float(__float_as_int(v) & (ok ? -1 : 0)); };
+
+  fetch(ts);
+  for (int t0 = ts; t0 < te; t0 += kChunk) {
+    // ---- take the prefetched chunk: owned-step values and staged B/C (zero outside the sequence / state range)
+    float cx[4], cu[4], cz[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bool ok = chv && (t0 + s * kSub + n) < te;
+      cx[s] = keep(ok, Buf<TI>::cvt(rx[s]));
+      cu[s] = keep(ok, Buf<TI>::cvt(rd[s]) + bias);
+      cz[s] = GATE ? keep(ok, Buf<TI>::cvt(rz[s])) : 0.0f;
+    }
+    float bv[4], cv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = nnv && (t0 + 4 * q + k) < te;
+      bv[k] = keep(ok, Buf<TI>::cvt(rb[k]));
+      cv[k] = AGG ? 0.0f : keep(ok, Buf<TI>::cvt(rc[k]));
+    }
+    __syncthreads();  // the previous chunk's readers of sB / sCt are done
+    *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+    if (!AGG) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sCt[4 * q + k][nn] = cv[k];
     }
     __syncthreads();
+    if (t0 + kChunk < te) fetch(t0 + kChunk);  // uniform; the loads land while this chunk is computed
 
+#pragma unroll
     for (int s = 0; s < kChunk / kSub; ++s) {
-      const int64_t tb = t0 + s * kSub;
+      const int tb = t0 + s * kSub;
       if (tb >= te) break;  // uniform across the workgroup
-      // ---- owned step: t = tb + n of channel d
-      const int64_t t = tb + n;
+      const int t = tb + n;
       const bool ev = chv && t < te;
-      const float xv = ev ? Elem<TI>::ld(xr, t) : 0.0f;
-      float zv = 0.0f;
-      if (GATE) zv = ev ? Elem<TI>::ld(zr, t) : 0.0f;
-      const float u = ev ? Elem<TI>::ld(dr, t) + bias : 0.0f;
-      float delta = p.softplus ? softplus(u) : u;
-      delta = ev ? delta : 0.0f;  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
+      const float xv = cx[s];
+      float delta = p.softplus ? softplus(cu[s]) : cu[s];
+      delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
       if (AGG) dsum += delta;
 
@@ -273,8 +360,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
           acc = fmaf(cc.w, hh.w, acc);
         }
         if (DSKIP) acc = fmaf(Dv, xv, acc);
-        if (GATE) acc *= silu(zv);
-        if (ev) Elem<TY>::st(yr, t, acc);
+        if (GATE) acc *= silu(cz[s]);
+        // out-of-range offset for steps outside the segment: the hardware drops the write
+        Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
       }
     }
   }
@@ -445,6 +533,9 @@ ssm_status check_common(const ssm_scan_params* p, bool need_seqlen) {
                        static_cast<double>(need_seqlen ? p->seqlen : 1) * 1.0;
   if (elems > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
   if (p->batch > 65535) return fail(SSM_ERR_SHAPE, "batch=%lld exceeds 65535", (long long)p->batch);
+  if (need_seqlen && p->seqlen > kMaxSeqlen)
+    return fail(SSM_ERR_SHAPE, "seqlen=%lld exceeds %lld (per-lane 32-bit buffer offsets)", (long long)p->seqlen,
+                (long long)kMaxSeqlen);
   if ((p->dim + 15) / 16 > 0x7fffffffLL) return fail(SSM_ERR_SHAPE, "dim too large");
   return SSM_OK;
 }

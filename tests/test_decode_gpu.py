@@ -43,7 +43,8 @@ def test_decode_equals_scan(io, disc, N):
         ys.append(ssm.state_update(state, sl("x"), sl("dt"), dd["A"], sl("B"), sl("C"), dt_bias=dd["dt_bias"],
                                    Dskip=dd["Dskip"], z=sl("z"), y_dtype=torch.float32, disc=disc))
     yd = torch.stack(ys, dim=2)
-    tol = 1e-6 if io == "f32" else 1e-5
+    # both sides are fp32 recurrences a few ulp from exact, with different summation orders
+    tol = 1e-5
     assert G.rel_max(G.to_np64(yd), G.to_np64(y_scan)) <= tol
     assert G.rel_max(G.to_np64(state), G.to_np64(h_scan)) <= tol
     # and against the oracle
