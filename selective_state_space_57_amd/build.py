@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libssm57.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-shared", "-Wall",
     # packed FP32 (v_pk_*_f32) stays off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

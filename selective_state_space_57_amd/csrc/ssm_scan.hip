@@ -119,13 +119,13 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + v) for v in [0, 1]: log(w) * v / (w - 1) with w = fl(1 + v) cancels the rounding of 1 + v (Goldberg,
-// "What every computer scientist should know about floating-point arithmetic", log1p via the correction factor).
+// log(1 + v) for v in [0, 1].  With w = fl(1 + v), the rounding error e = (w - 1) - v is exact (Sterbenz) and
+// log(1 + v) = log(w) - e / w + O(e^2).  |e| <= 2^-24, so 1/w may be replaced by (1 - v) (relative difference v^2):
+// log1p(v) = log(w) + (v - (w - 1)) * (1 - v), accurate to a few ulp with no division or branch (w == 1 gives v).
 __device__ __forceinline__ float log1p_01(float v) {
-  float w = 1.0f + v;
-  float wm1 = w - 1.0f;
-  float r = hw_log2(w) * kLn2 * (v * hw_rcp(wm1));
-  return wm1 == 0.0f ? v : r;
+  const float w = 1.0f + v;
+  const float c = v - (w - 1.0f);
+  return fmaf(c, 1.0f - v, hw_log2(w) * kLn2);
 }
 
 // softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e^-|u|)   (tau_Delta of paper section 3.2)
@@ -166,6 +166,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// single-dword LDS write that the compiler cannot merge with its neighbours into a two-dword write
+template <int OFF>
+__device__ __forceinline__ void lds_write_b32(uint32_t lds_addr, float v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(lds_addr), "v"(v), "i"(OFF) : "memory");
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -198,7 +204,8 @@ struct ScanArgs {
 // Delta and Delta*x, contracting with C and storing y, plus four B and four C values it stages into LDS.  All of
 // these global loads are issued one chunk ahead, so their latency hides behind a whole chunk of arithmetic.
 template <typename TI, typename TY, bool ZOH, bool AGG, bool GATE, bool DSKIP>
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
+// five resident workgroups per CU (<= 96 VGPRs): a 4 x 5120-channel layer is exactly 5 workgroups per CU
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void scan_kernel(ScanArgs p) {
   __shared__ __align__(16) float sB[kChanPerWG][kBStride];           // B_n(t) of the chunk, [n][t]
   __shared__ __align__(16) float sCt[AGG ? 1 : kChunk][kCtStride];   // C_n(t) of the chunk, [t][n]
   __shared__ __align__(16) float sH[AGG ? 1 : kChanPerWG * kHRow];   // states of a 16-step block, per row [t][n]
@@ -234,6 +241,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
   const uint32_t lane_xo = (static_cast<uint32_t>(row) * static_cast<uint32_t>(L) + n) * SI;  // + t0 * SI
   const uint32_t lane_yo = (static_cast<uint32_t>(row) * static_cast<uint32_t>(L) + n) * SY;
   const uint32_t lane_bo = (static_cast<uint32_t>(nn) * static_cast<uint32_t>(L) + 4 * q) * SI;
+  // C staging role: step ct of the chunk, states 4 cg .. 4 cg + 3 (consecutive lanes write consecutive LDS rows)
+  const int ct = tid & 63, cg = tid >> 6;
+  const uint32_t lane_co = (static_cast<uint32_t>(4 * cg) * static_cast<uint32_t>(L) + ct) * SI;
 
   const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
   const float Ap = An * kLog2e;                                   // exp(Delta*A) = exp2(Delta*A*log2(e))
@@ -255,59 +265,56 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
   // or the row are masked off below.
   using Raw = typename Buf<TI>::Raw;
   Raw rx[4], rd[4], rz[4], rb[4], rc[4];
-  auto fetch = [&](int t0) {
-    const uint32_t xo = lane_xo + static_cast<uint32_t>(t0) * SI;
+  auto fetch_owned = [&](int t0, int s) {  // x, dt, z of step t0 + 16 s + n
+    const uint32_t xo = lane_xo + static_cast<uint32_t>(t0 + s * kSub) * SI;
+    rx[s] = Buf<TI>::ld(rx_, xo);
+    rd[s] = Buf<TI>::ld(rd_, xo);
+    if (GATE) rz[s] = Buf<TI>::ld(rz_, xo);
+  };
+  auto fetch_staged = [&](int t0) {  // B (steps 4q..4q+3 of state nn) and C (step ct of states 4cg..4cg+3)
     const uint32_t bo = lane_bo + static_cast<uint32_t>(t0) * SI;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      rx[s] = Buf<TI>::ld(rx_, xo + s * kSub * SI);
-      rd[s] = Buf<TI>::ld(rd_, xo + s * kSub * SI);
-      if (GATE) rz[s] = Buf<TI>::ld(rz_, xo + s * kSub * SI);
-    }
+    const uint32_t co = lane_co + static_cast<uint32_t>(t0) * SI;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       rb[k] = Buf<TI>::ld(rb_, bo + k * SI);
-      if (!AGG) rc[k] = Buf<TI>::ld(rc_, bo + k * SI);
+      if (!AGG) rc[k] = Buf<TI>::ld(rc_, co + static_cast<uint32_t>(k) * static_cast<uint32_t>(L) * SI);
     }
   };
   // zero a value unless `ok` (bitwise, so that whatever was read at a clamped index cannot leak in)
   auto keep = [](bool ok, float v) { return __int_as_float(__float_as_int(v) & (ok ? -1 : 0)); };
 
-  fetch(ts);
-  for (int t0 = ts; t0 < te; t0 += kChunk) {
-    // ---- take the prefetched chunk: owned-step values and staged B/C (zero outside the sequence / state range)
-    float cx[4], cu[4], cz[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bool ok = chv && (t0 + s * kSub + n) < te;
-      cx[s] = keep(ok, Buf<TI>::cvt(rx[s]));
-      cu[s] = keep(ok, Buf<TI>::cvt(rd[s]) + bias);
-      cz[s] = GATE ? keep(ok, Buf<TI>::cvt(rz[s])) : 0.0f;
-    }
+  const bool wg_full = static_cast<int64_t>(blockIdx.x) * kChanPerWG + kChanPerWG <= p.dim && p.N == kSub;
+
+  // one 64-step chunk; FULL: every step and every channel / state of the workgroup is valid, so no masking
+  auto chunk = [&]<bool FULL>(int t0) {
+    // ---- stage the prefetched B and C of this chunk (zero outside the sequence / state range)
     float bv[4], cv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const bool ok = nnv && (t0 + 4 * q + k) < te;
-      bv[k] = keep(ok, Buf<TI>::cvt(rb[k]));
-      cv[k] = AGG ? 0.0f : keep(ok, Buf<TI>::cvt(rc[k]));
+      const bool okb = FULL || (nnv && (t0 + 4 * q + k) < te);
+      const bool okc = FULL || ((4 * cg + k) < p.N && (t0 + ct) < te);
+      bv[k] = keep(okb, Buf<TI>::cvt(rb[k]));
+      cv[k] = AGG ? 0.0f : keep(okc, Buf<TI>::cvt(rc[k]));
     }
     __syncthreads();  // the previous chunk's readers of sB / sCt are done
     *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
-    if (!AGG) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sCt[4 * q + k][nn] = cv[k];
-    }
+    if (!AGG) *reinterpret_cast<float4*>(&sCt[ct][4 * cg]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
     __syncthreads();
-    if (t0 + kChunk < te) fetch(t0 + kChunk);  // uniform; the loads land while this chunk is computed
+    const bool more = t0 + kChunk < te;  // uniform
+    if (more) fetch_staged(t0 + kChunk);
 
 #pragma unroll
     for (int s = 0; s < kChunk / kSub; ++s) {
       const int tb = t0 + s * kSub;
-      if (tb >= te) break;  // uniform across the workgroup
+      if (!FULL && tb >= te) break;  // uniform across the workgroup
       const int t = tb + n;
-      const bool ev = chv && t < te;
-      const float xv = cx[s];
-      float delta = p.softplus ? softplus(cu[s]) : cu[s];
+      const bool ev = FULL || (chv && t < te);
+      // ---- this lane's owned step: convert it, then reuse its registers for the same block of the next chunk
+      const float xv = keep(ev, Buf<TI>::cvt(rx[s]));
+      const float uv = keep(ev, Buf<TI>::cvt(rd[s]) + bias);
+      const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s])) : 0.0f;
+      if (more) fetch_owned(t0 + kChunk, s);
+      float delta = p.softplus ? softplus(uv) : uv;
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
       if (AGG) dsum += delta;
@@ -323,8 +330,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
         bq[4 * i + 3] = v.w;
       }
 
-      // ---- 16 sequential steps of the recurrence for this lane's state
-      float hv[kSub];
+      // ---- 16 sequential steps of the recurrence for this lane's state; each new state goes straight to LDS
+      // (single-dword writes: 64 lanes on 64 distinct banks) for the transposition below
+      if (!AGG) wave_lds_sync();  // the previous block's gathers of this row are done
+      const uint32_t hw_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(hrow + n));
       static_for<kSub>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         const float dk = row_bcast<k>(delta);
@@ -338,14 +347,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
           bb = row_bcast<k>(dx) * bq[k];
         }
         h = fmaf(a, h, bb);
-        hv[k] = h;
+        if (!AGG) lds_write_b32<k * kCtStride * 4>(hw_addr, h);
       });
 
       if (!AGG) {
         // ---- transpose through LDS: lane j of the row gathers h_n(tb + j) for all n and contracts with C
-        wave_lds_sync();
-#pragma unroll
-        for (int k = 0; k < kSub; ++k) hrow[k * kCtStride + n] = hv[k];
         wave_lds_sync();
         float acc = 0.0f;
         const float* hs = &hrow[n * kCtStride];
@@ -360,11 +366,21 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
           acc = fmaf(cc.w, hh.w, acc);
         }
         if (DSKIP) acc = fmaf(Dv, xv, acc);
-        if (GATE) acc *= silu(cz[s]);
+        if (GATE) acc *= silu(zv);
         // out-of-range offset for steps outside the segment: the hardware drops the write
         Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
       }
     }
+  };
+
+  fetch_staged(ts);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fetch_owned(ts, s);
+  for (int t0 = ts; t0 < te; t0 += kChunk) {
+    if (wg_full && t0 + kChunk <= te)
+      chunk.template operator()<true>(t0);
+    else
+      chunk.template operator()<false>(t0);
   }
 
   if (AGG) {
@@ -403,8 +419,11 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
 }
 
 // ---------------------------------------------------------------------------------------------------------------
-// Decode: one step per (batch, channel).  HBM-bound (the fp32 state is read and written once), so the layout is
-// chosen for coalescing: a quad of lanes owns one channel, each lane four consecutive states (one 16-byte access).
+// Decode: one step per (batch, channel).  HBM-bound: the fp32 state is read and written once, so the layout is chosen
+// for coalescing.  A quad of lanes owns one channel, lane q its states 4q .. 4q+3, so consecutive lanes touch
+// consecutive 16-byte pieces of the state (a wave reads and writes 1 KB contiguous per instruction).  Each lane
+// fetches its four B and C values with one 8-byte load each, the quad sums its partial C-contractions with two DPP
+// adds, and lane 0 of the quad finishes y.  A thread handles kDecodeBatches batches, loading everything first.
 struct DecodeArgs {
   float* state;
   const void* x;
@@ -420,79 +439,114 @@ struct DecodeArgs {
   int N, softplus;
 };
 
+constexpr int kDecodeBatches = 2;
+
+// four consecutive elements starting at a multiple of 4 (vector path: N == 16, aligned)
+template <typename T>
+__device__ __forceinline__ void ld4(const T* p, float out[4]);
+template <>
+__device__ __forceinline__ void ld4<float>(const float* p, float out[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void ld4<uint16_t>(const uint16_t* p, float out[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(v.x << 16);
+  out[1] = __uint_as_float(v.x & 0xffff0000u);
+  out[2] = __uint_as_float(v.y << 16);
+  out[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
 template <typename TI, typename TY, bool ZOH, bool VEC>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   const int tid = threadIdx.x;
   const int q = tid & 3;
   const int64_t d = static_cast<int64_t>(blockIdx.x) * 64 + (tid >> 2);
-  const int64_t b = blockIdx.y;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kDecodeBatches;
   const bool chv = d < p.dim;
-  const int64_t ch = b * p.dim + d;
-  float xv = 0.0f, u = 0.0f, zv = 0.0f;
-  if (chv) {
-    xv = Elem<TI>::ld(static_cast<const TI*>(p.x), ch);
-    u = Elem<TI>::ld(static_cast<const TI*>(p.dt), ch) + (p.dt_bias ? p.dt_bias[d] : 0.0f);
-    if (p.z) zv = Elem<TI>::ld(static_cast<const TI*>(p.z), ch);
-  }
-  const float delta = p.softplus ? softplus(u) : u;
-  const float dx = delta * xv;
-  const TI* Bb = static_cast<const TI*>(p.B) + b * p.N;
-  const TI* Cb = static_cast<const TI*>(p.C) + b * p.N;
-  float hs[4], As[4];
+  float As[4];
   if (VEC) {
     if (chv) {
-      const float4 hv = *reinterpret_cast<const float4*>(p.state + ch * 16 + 4 * q);
       const float4 av = *reinterpret_cast<const float4*>(p.A + d * 16 + 4 * q);
-      hs[0] = hv.x; hs[1] = hv.y; hs[2] = hv.z; hs[3] = hv.w;
       As[0] = av.x; As[1] = av.y; As[2] = av.z; As[3] = av.w;
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hs[i] = As[i] = 0.0f;
+      As[0] = As[1] = As[2] = As[3] = 0.0f;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nn = 4 * q + i;
-      const bool ok = chv && nn < p.N;
-      hs[i] = ok ? p.state[ch * p.N + nn] : 0.0f;
-      As[i] = ok ? p.A[d * p.N + nn] : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) As[i] = (chv && 4 * q + i < p.N) ? p.A[d * p.N + 4 * q + i] : 0.0f;
   }
-  float acc = 0.0f;
+  const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
+  const float Dv = (chv && p.Dskip) ? p.Dskip[d] : 0.0f;
+
+  float hs[kDecodeBatches][4], Bv[kDecodeBatches][4], Cv[kDecodeBatches][4];
+  float xv[kDecodeBatches], uv[kDecodeBatches], zv[kDecodeBatches];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nn = 4 * q + i;
-    const bool ok = nn < p.N;
-    const float Bn = ok ? Elem<TI>::ld(Bb, nn) : 0.0f;
-    const float Cn = ok ? Elem<TI>::ld(Cb, nn) : 0.0f;
-    const float a = hw_exp2(delta * (As[i] * kLog2e));
-    float bb;
-    if (ZOH) {
-      const float en = delta * As[i];
-      const float coef = As[i] != 0.0f ? expm1_from(en, a) * (1.0f / As[i]) : delta;
-      bb = coef * Bn * xv;
+  for (int j = 0; j < kDecodeBatches; ++j) {
+    const int64_t b = b0 + j;
+    const bool bv = b < p.batch;
+    const bool ok = chv && bv;
+    const int64_t ch = b * p.dim + d;
+    const int64_t bb = bv ? b : 0;
+    xv[j] = ok ? Elem<TI>::ld(static_cast<const TI*>(p.x), ch) : 0.0f;
+    uv[j] = ok ? Elem<TI>::ld(static_cast<const TI*>(p.dt), ch) + bias : 0.0f;
+    zv[j] = (ok && p.z) ? Elem<TI>::ld(static_cast<const TI*>(p.z), ch) : 0.0f;
+    if (VEC) {
+      if (ok) {
+        const float4 hv = *reinterpret_cast<const float4*>(p.state + ch * 16 + 4 * q);
+        hs[j][0] = hv.x; hs[j][1] = hv.y; hs[j][2] = hv.z; hs[j][3] = hv.w;
+      } else {
+        hs[j][0] = hs[j][1] = hs[j][2] = hs[j][3] = 0.0f;
+      }
+      ld4<TI>(static_cast<const TI*>(p.B) + bb * 16 + 4 * q, Bv[j]);
+      ld4<TI>(static_cast<const TI*>(p.C) + bb * 16 + 4 * q, Cv[j]);
     } else {
-      bb = dx * Bn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nn = 4 * q + i;
+        hs[j][i] = (ok && nn < p.N) ? p.state[ch * p.N + nn] : 0.0f;
+        Bv[j][i] = nn < p.N ? Elem<TI>::ld(static_cast<const TI*>(p.B), bb * p.N + nn) : 0.0f;
+        Cv[j][i] = nn < p.N ? Elem<TI>::ld(static_cast<const TI*>(p.C), bb * p.N + nn) : 0.0f;
+      }
     }
-    hs[i] = fmaf(a, hs[i], bb);
-    acc = fmaf(Cn, hs[i], acc);
   }
-  // sum over the quad (DPP quad_perm)
-  acc += __shfl_xor(acc, 1, 4);
-  acc += __shfl_xor(acc, 2, 4);
-  if (VEC) {
-    if (chv) *reinterpret_cast<float4*>(p.state + ch * 16 + 4 * q) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-  } else {
+#pragma unroll
+  for (int j = 0; j < kDecodeBatches; ++j) {
+    const int64_t b = b0 + j;
+    const bool ok = chv && b < p.batch;
+    const int64_t ch = b * p.dim + d;
+    const float delta = p.softplus ? softplus(uv[j]) : uv[j];
+    const float dx = delta * xv[j];
+    float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int nn = 4 * q + i;
-      if (chv && nn < p.N) p.state[ch * p.N + nn] = hs[i];
+      const float a = hw_exp2(delta * (As[i] * kLog2e));
+      float bbar;
+      if (ZOH) {
+        const float en = delta * As[i];
+        const float coef = As[i] != 0.0f ? expm1_from(en, a) * (1.0f / As[i]) : delta;
+        bbar = coef * Bv[j][i] * xv[j];
+      } else {
+        bbar = dx * Bv[j][i];
+      }
+      hs[j][i] = fmaf(a, hs[j][i], bbar);
+      acc = fmaf(Cv[j][i], hs[j][i], acc);
     }
-  }
-  if (chv && q == 0) {
-    if (p.Dskip) acc = fmaf(p.Dskip[d], xv, acc);
-    if (p.z) acc *= silu(zv);
-    Elem<TY>::st(static_cast<TY*>(p.y), ch, acc);
+    acc += __shfl_xor(acc, 1, 4);  // sum over the quad
+    acc += __shfl_xor(acc, 2, 4);
+    if (VEC) {
+      if (ok) *reinterpret_cast<float4*>(p.state + ch * 16 + 4 * q) = make_float4(hs[j][0], hs[j][1], hs[j][2], hs[j][3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (ok && 4 * q + i < p.N) p.state[ch * p.N + 4 * q + i] = hs[j][i];
+    }
+    if (ok && q == 0) {
+      if (p.Dskip) acc = fmaf(Dv, xv[j], acc);
+      if (p.z) acc *= silu(zv[j]);
+      Elem<TY>::st(static_cast<TY*>(p.y), ch, acc);
+    }
   }
 }
 
@@ -695,8 +749,9 @@ ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* 
   DecodeArgs a{};
   a.state = state; a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z;
   a.y = y; a.batch = p->batch; a.dim = p->dim; a.N = static_cast<int>(p->dstate); a.softplus = p->dt_softplus;
-  const bool vec = p->dstate == 16 && aligned(state, 16) && aligned(A, 16);
-  const dim3 grid(static_cast<unsigned>((p->dim + 63) / 64), static_cast<unsigned>(p->batch));
+  const bool vec = p->dstate == 16 && aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * io) && aligned(C, 4 * io);
+  const dim3 grid(static_cast<unsigned>((p->dim + 63) / 64),
+                  static_cast<unsigned>((p->batch + kDecodeBatches - 1) / kDecodeBatches));
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = p->io_dtype == SSM_F32 ? launch_decode_io<float>(a, grid, st, p, vec)
                                               : launch_decode_io<uint16_t>(a, grid, st, p, vec);
