@@ -55,16 +55,22 @@ def src_hash():
 
 
 def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch (read + written) from the committed rocprofv3 counter record, if it was taken on the
+    current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
     try:
-        with open(path) as f:
-            rec = json.load(f).get(kernel_key)
-    except (OSError, ValueError):
+        lines = open(path).read().splitlines()
+    except OSError:
         return None
-    if not rec or rec.get("src_hash") != src_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    for line in lines:
+        if line.startswith("#") or "|" not in line:
+            continue
+        f = [x.strip() for x in line.split("|")]
+        if len(f) == 4 and f[0] == kernel_key:
+            if f[1] != src_hash():
+                return None
+            return int(f[2]) + int(f[3])
+    return None
 
 
 def host_cores():
@@ -211,6 +217,8 @@ def main():
         dbytes = decode_algorithmic_bytes(wd.batch, wd.dim, wd.dstate)
         out["decode"] = {"workload": "decode-b256-d5120", "steps": wd.decode_steps, "us_per_step": dms * 1e3,
                          "algorithmic_bytes_per_step": dbytes, "achieved_GBps": dbytes / (dms * 1e-3) / 1e9,
+                         "frac_of_8TBps": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_kernel<bf16,bf16,euler,vec> decode-b256-d5120"),
                          "note": "64 consecutive steps, each with its own pre-generated x/dt/z/B/C tensors; the 84 MB "
                                  "fp32 state can be partly served by the 256 MB Infinity Cache"}
 
