@@ -264,12 +264,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   // raw (unconverted) prefetch registers for one chunk.  Reads past the tensors return 0; reads past the segment
   // or the row are masked off below.
   using Raw = typename Buf<TI>::Raw;
-  Raw rx[4], rd[4], rz[4], rb[4], rc[4];
-  auto fetch_owned = [&](int t0, int s) {  // x, dt, z of step t0 + 16 s + n
-    const uint32_t xo = lane_xo + static_cast<uint32_t>(t0 + s * kSub) * SI;
-    rx[s] = Buf<TI>::ld(rx_, xo);
-    rd[s] = Buf<TI>::ld(rd_, xo);
-    if (GATE) rz[s] = Buf<TI>::ld(rz_, xo);
+  // owned x/dt/z are fetched two 16-step blocks ahead through a ring of two slots; B/C one chunk ahead
+  Raw rx[2], rd[2], rz[2], rb[4], rc[4];
+  auto fetch_owned = [&](int tb, int slot) {  // x, dt, z of step tb + n into ring slot `slot`
+    const uint32_t xo = lane_xo + static_cast<uint32_t>(tb) * SI;
+    rx[slot] = Buf<TI>::ld(rx_, xo);
+    rd[slot] = Buf<TI>::ld(rd_, xo);
+    if (GATE) rz[slot] = Buf<TI>::ld(rz_, xo);
   };
   auto fetch_staged = [&](int t0) {  // B (steps 4q..4q+3 of state nn) and C (step ct of states 4cg..4cg+3)
     const uint32_t bo = lane_bo + static_cast<uint32_t>(t0) * SI;
@@ -309,11 +310,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       if (!FULL && tb >= te) break;  // uniform across the workgroup
       const int t = tb + n;
       const bool ev = FULL || (chv && t < te);
-      // ---- this lane's owned step: convert it, then reuse its registers for the same block of the next chunk
-      const float xv = keep(ev, Buf<TI>::cvt(rx[s]));
-      const float uv = keep(ev, Buf<TI>::cvt(rd[s]) + bias);
-      const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s])) : 0.0f;
-      if (more) fetch_owned(t0 + kChunk, s);
+      // ---- this lane's owned step: convert it, then reuse its ring slot for the block two ahead
+      const float xv = keep(ev, Buf<TI>::cvt(rx[s & 1]));
+      const float uv = keep(ev, Buf<TI>::cvt(rd[s & 1]) + bias);
+      const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s & 1])) : 0.0f;
+      if (tb + 2 * kSub < te) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
       float delta = p.softplus ? softplus(uv) : uv;
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   };
 
   fetch_staged(ts);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) fetch_owned(ts, s);
+  fetch_owned(ts, 0);
+  if (ts + kSub < te) fetch_owned(ts + kSub, 1);
   for (int t0 = ts; t0 < te; t0 += kChunk) {
     if (wg_full && t0 + kChunk <= te)
       chunk.template operator()<true>(t0);
