@@ -11,7 +11,9 @@ y = C h + D x and the optional SiLU gate of the Mamba block (ifdog.com tutorial,
 
 Pins (tests/test_oracle_pins.py) tie it to closed forms: the LTI convolution kernel, Theorem 1's gated RNN, the
 cumulative-sum (materialised) form, tree scans with the associative combine, split-sequence hand-off, linearity,
-reset/hold limits, the ZOH-to-Euler ratio and decode == scan.
+reset/hold limits, the ZOH-to-Euler ratio and decode == scan.  The backward (``scan_bwd``, the chain rule through
+that definition) is pinned by central finite differences of the forward, element by element, for both discretisations,
+including A = 0 and the small-|Delta A| series branch.
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def _bind(path: str):
     lib.oracle_state_update_f64.argtypes = [I64, I64, I64, I, I] + [P] * 10 + [I]
     lib.oracle_state_update_f64.restype = I
     lib.oracle_max_threads.restype = I
+    lib.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64, I, I] + [P] * 20 + [I]
+    lib.oracle_scan_bwd_f64.restype = I
     return lib
 
 
@@ -130,6 +134,36 @@ def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, disc=E
     return y, st
 
 
+def scan_bwd(x, dt, A, B, C, dy, dt_bias=None, Dskip=None, z=None, h0=None, dh_final=None, disc=EULER_B,
+             softplus=True, nthreads=0, _lib_override=None):
+    """Gradients of the scan.  Returns a dict: dx, ddt, dz (b, D, L); dB, dC (b, N, L); dA (D, N); dD, ddt_bias (D,);
+    dh0 (b, D, N).  dz / dD / ddt_bias are zeros when the gate / D / bias are absent."""
+    x = _f64(x)
+    bsz, dim, L = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _f64(dt, (bsz, dim, L))
+    B = _f64(B, (bsz, N, L))
+    C = _f64(C, (bsz, N, L))
+    dy = _f64(dy, (bsz, dim, L))
+    dt_bias = _f64(dt_bias, (dim,))
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, (bsz, dim, L))
+    h0 = _f64(h0, (bsz, dim, N))
+    dh_final = _f64(dh_final, (bsz, dim, N))
+    out = {"dx": np.zeros((bsz, dim, L)), "ddt": np.zeros((bsz, dim, L)), "dz": np.zeros((bsz, dim, L)),
+           "dB": np.zeros((bsz, N, L)), "dC": np.zeros((bsz, N, L)), "dA": np.zeros((dim, N)),
+           "dD": np.zeros(dim), "ddt_bias": np.zeros(dim), "dh0": np.zeros((bsz, dim, N))}
+    rc = (_lib_override or _load()).oracle_scan_bwd_f64(
+        bsz, dim, L, N, int(disc), int(bool(softplus)), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+        _ptr(out["ddt_bias"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+        _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd_f64 failed with code %d" % rc)
+    return out
+
+
 class Oracle:
     """The oracle bound to a specific compiled library (the default one, or a test-built variant)."""
 
@@ -141,6 +175,9 @@ class Oracle:
 
     def state_update(self, *a, **k):
         return state_update(*a, _lib_override=self._lib, **k)
+
+    def scan_bwd(self, *a, **k):
+        return scan_bwd(*a, _lib_override=self._lib, **k)
 
 
 def compile_variant(src_text: str, out_path: str) -> str:

@@ -29,6 +29,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #ifdef _OPENMP
 #include <omp.h>
@@ -116,6 +117,162 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, int disc
                  z ? z[ch] : 0.0, state + ch * dstate);
   }
   return 0;
+}
+
+/*
+ * Backward of the scan (gradients of a scalar loss given dL/dy and optionally dL/dh_final), fp64.
+ * The training path needs these gradients (Mamba paper, section 3.3.2, the recomputation paragraph: the backward pass
+ * of the fused layer rebuilds the states from the inputs; alishangtian.com close reading, "hardware-aware algorithm",
+ * item on recomputation).  They are the chain rule through the forward definition above, nothing more.
+ * Recomputation is not needed here: the oracle keeps every state h_t of a channel.  Per channel, walking t from
+ * L-1 down to 0 with the adjoint g = dL/dh_t:
+ *   s_t = sum_n C h_t + D x_t (pre-gate output),  ds = dy * silu(z) (dy without gate),  dz = dy * s * silu'(z)
+ *   g  += C_t * ds;  then with a = exp(Delta A), b-coefficient coef (Delta for Euler-B, expm1(Delta A)/A for ZOH):
+ *   dDelta += g (d coef/dDelta B x + h_{t-1} a A),  dx += g coef B,  dB += g coef x,  dC += ds h_t,
+ *   dA += g (d coef/dA B x + h_{t-1} a Delta),  g *= a  (adjoint of h_{t-1});   dx += ds D,  dD += ds x,
+ *   du = dDelta * sigmoid(u) (softplus derivative; 1 when softplus is off),  ddt = du,  dbias += du,
+ *   finally dh0 = g.
+ * Layouts as the forward; dB, dC [b][N][L] (summed over channels), dA [D][N], dD, dbias [D] (summed over b, t).
+ * Work is split over batch elements (each thread owns its batch's dB / dC); per-channel parameter gradients are
+ * accumulated per batch element and summed afterwards in a fixed order, so results do not depend on threads.
+ */
+static double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int disc, int use_softplus,
+                        const double* x, const double* dt, const double* dt_bias, const double* A, const double* B,
+                        const double* C, const double* Dskip, const double* z, const double* h0, const double* dy,
+                        const double* dh_final, double* dx, double* ddt, double* ddt_bias, double* dA, double* dB,
+                        double* dC, double* dD, double* dz, double* dh0, int nthreads) {
+  if (batch < 0 || dim < 0 || seqlen < 1 || dstate < 1 || dstate > 4096) return 1;
+  if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t N = dstate, L = seqlen;
+  /* per-batch partials of the per-channel parameter gradients */
+  double* pA = (double*)calloc((size_t)(batch * dim * N), sizeof(double));
+  double* pD = (double*)calloc((size_t)(batch * dim), sizeof(double));
+  double* pb = (double*)calloc((size_t)(batch * dim), sizeof(double));
+  if (!pA || !pD || !pb) {
+    free(pA); free(pD); free(pb);
+    return 3;
+  }
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < batch; b++) {
+    double* H = (double*)malloc((size_t)((L + 1) * N) * sizeof(double)); /* H[t+1] = h_t, H[0] = h0 */
+    double* Dl = (double*)malloc((size_t)L * sizeof(double));
+    double* S = (double*)malloc((size_t)L * sizeof(double));
+    double* g = (double*)malloc((size_t)N * sizeof(double));
+    if (!H || !Dl || !S || !g) {
+#pragma omp atomic write
+      failed = 1;
+      free(H); free(Dl); free(S); free(g);
+      continue;
+    }
+    for (int64_t i = 0; i < N * L; i++) {
+      dB[b * N * L + i] = 0.0;
+      dC[b * N * L + i] = 0.0;
+    }
+    for (int64_t d = 0; d < dim; d++) {
+      const int64_t ch = b * dim + d;
+      const double* xr = x + ch * L;
+      const double* dr = dt + ch * L;
+      const double* Bb = B + b * N * L;
+      const double* Cb = C + b * N * L;
+      const double* Ar = A + d * N;
+      const double bias = dt_bias ? dt_bias[d] : 0.0;
+      const double Dv = Dskip ? Dskip[d] : 0.0;
+      /* forward, keeping every state */
+      for (int64_t n = 0; n < N; n++) H[n] = h0 ? h0[ch * N + n] : 0.0;
+      for (int64_t t = 0; t < L; t++) {
+        const double u = dr[t] + bias;
+        const double delta = use_softplus ? sp(u) : u;
+        Dl[t] = delta;
+        double s = 0.0;
+        for (int64_t n = 0; n < N; n++) {
+          const double An = Ar[n];
+          const double abar = exp(delta * An);
+          const double coef = (disc == 0) ? delta : (An == 0.0 ? delta : expm1(delta * An) / An);
+          H[(t + 1) * N + n] = abar * H[t * N + n] + coef * Bb[n * L + t] * xr[t];
+          s += Cb[n * L + t] * H[(t + 1) * N + n];
+        }
+        S[t] = s + Dv * xr[t];
+      }
+      /* backward */
+      for (int64_t n = 0; n < N; n++) g[n] = dh_final ? dh_final[ch * N + n] : 0.0;
+      double accD = 0.0, accb = 0.0;
+      for (int64_t t = L - 1; t >= 0; t--) {
+        const double xv = xr[t], dyv = dy[ch * L + t], delta = Dl[t];
+        double ds = dyv;
+        if (z) {
+          const double zv = z[ch * L + t], sg = sigm(zv);
+          ds = dyv * zv * sg;
+          if (dz) dz[ch * L + t] = dyv * S[t] * (sg * (1.0 + zv * (1.0 - sg)));
+        } else if (dz) {
+          dz[ch * L + t] = 0.0;
+        }
+        double dDelta = 0.0, dxv = ds * Dv;
+        accD += ds * xv;
+        for (int64_t n = 0; n < N; n++) {
+          const double An = Ar[n], Bv = Bb[n * L + t], Cv = Cb[n * L + t];
+          const double hprev = H[t * N + n], hcur = H[(t + 1) * N + n];
+          const double abar = exp(delta * An);
+          g[n] += Cv * ds;
+          dC[b * N * L + n * L + t] += ds * hcur;
+          double coef, dcoef_dd, dcoef_dA;
+          if (disc == 0) {
+            coef = delta; dcoef_dd = 1.0; dcoef_dA = 0.0;
+          } else if (An == 0.0) {
+            coef = delta; dcoef_dd = 1.0; dcoef_dA = 0.5 * delta * delta;
+          } else {
+            const double e = delta * An;
+            coef = expm1(e) / An;
+            dcoef_dd = abar;
+            if (fabs(e) < 1e-3) /* (x e^x - e^x + 1) / x^2 = 1/2 + x/3 + x^2/8 + x^3/30 + ... */
+              dcoef_dA = delta * delta * (0.5 + e * (1.0 / 3.0 + e * (1.0 / 8.0 + e * (1.0 / 30.0))));
+            else
+              dcoef_dA = (delta * abar - coef) / An;
+          }
+          dDelta += g[n] * (dcoef_dd * Bv * xv + hprev * abar * An);
+          dxv += g[n] * coef * Bv;
+          dB[b * N * L + n * L + t] += g[n] * coef * xv;
+          pA[ch * N + n] += g[n] * (dcoef_dA * Bv * xv + hprev * abar * delta);
+          g[n] *= abar;
+        }
+        const double u = dr[t] + bias;
+        const double du = use_softplus ? dDelta * sigm(u) : dDelta;
+        ddt[ch * L + t] = du;
+        dx[ch * L + t] = dxv;
+        accb += du;
+      }
+      pD[ch] = accD;
+      pb[ch] = accb;
+      if (dh0)
+        for (int64_t n = 0; n < N; n++) dh0[ch * N + n] = g[n];
+    }
+    free(H); free(Dl); free(S); free(g);
+  }
+  if (!failed) {
+    for (int64_t d = 0; d < dim; d++) {
+      double sD = 0.0, sb = 0.0;
+      for (int64_t b = 0; b < batch; b++) {
+        sD += pD[b * dim + d];
+        sb += pb[b * dim + d];
+      }
+      if (dD) dD[d] = sD;
+      if (ddt_bias) ddt_bias[d] = sb;
+      for (int64_t n = 0; n < N; n++) {
+        double sa = 0.0;
+        for (int64_t b = 0; b < batch; b++) sa += pA[(b * dim + d) * N + n];
+        dA[d * N + n] = sa;
+      }
+    }
+  }
+  free(pA); free(pD); free(pb);
+  return failed ? 3 : 0;
 }
 
 int oracle_max_threads(void) {

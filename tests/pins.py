@@ -288,6 +288,44 @@ def pin_worked_examples(orc, rows):
         assert abs(hf[0, 0, 0] - row["h"]) < 1e-14 * max(1, abs(row["h"])), (row["name"], hf[0, 0, 0], row["h"])
 
 
+# P10: backward = central finite differences of the (pinned) forward oracle, for every input element.  The loss is
+#      sum(dy * y) + sum(dh_final * h_final) with random weights; every gradient the backward returns is checked.
+def pin_bwd_finite_differences(orc, disc, seed=10):
+    c = _case(1000 + seed + disc, b=2, D=3, L=9, N=4)
+    r = _rng(1100 + seed + disc)
+    if disc == ZOH:
+        c["A"] = c["A"].copy()
+        c["A"][0, 0] = 0.0      # A == 0 limit
+        c["A"][1, 1] = -6e-4    # |Delta A| just under 1e-3: series branch of the A-derivative, where its terms matter
+        c["A"][2, 2] = -1e-5    # tiny |Delta A|
+    dy = r.standard_normal(c["x"].shape)
+    dhf = r.standard_normal(c["h0"].shape)
+    g = orc.scan_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], dy, dt_bias=c["dt_bias"], Dskip=c["Dskip"], z=c["z"],
+                     h0=c["h0"], dh_final=dhf, disc=disc)
+
+    def loss(cc):
+        y, hf = orc.scan(**cc, disc=disc)
+        return float(np.sum(dy * y) + np.sum(dhf * hf))
+
+    names = {"x": "dx", "dt": "ddt", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "Dskip": "dD", "dt_bias": "ddt_bias",
+             "h0": "dh0"}
+    for key, gk in names.items():
+        base = c[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[idx]))
+            cp = dict(c)
+            v = base.copy()
+            v[idx] = base[idx] + eps
+            cp[key] = v
+            lp = loss(cp)
+            v[idx] = base[idx] - eps
+            lm = loss(cp)
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - g[gk])) / max(1.0, float(np.max(np.abs(fd))))
+        assert err < 2e-6, ("P10", disc, gk, err)
+
+
 def all_pins(orc, worked_rows):
     """Run every pin; returns a list of (name, error-or-None)."""
     out = []
@@ -301,7 +339,8 @@ def all_pins(orc, worked_rows):
                    ("associative_%d" % disc, lambda disc=disc: pin_associative(orc, disc)),
                    ("linearity_%d" % disc, lambda disc=disc: pin_linearity(orc, disc)),
                    ("reset_hold_%d" % disc, lambda disc=disc: pin_reset_hold(orc, disc)),
-                   ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc))]
+                   ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
+                   ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
     for name, fn in checks:
         try:
             fn()

@@ -55,6 +55,28 @@ def test_identity(orc, name, disc):
     getattr(pins, "pin_" + name)(orc, disc)
 
 
+@pytest.mark.parametrize("disc", [pins.EULER_B, pins.ZOH])
+def test_backward_finite_differences(orc, disc):
+    pins.pin_bwd_finite_differences(orc, disc)
+
+
+def test_backward_without_optional_parts(orc):
+    # no gate / D / bias / h0 / dh_final: dz is zero, dD is the gradient at D = 0 (sum of dy * x), and the rest still
+    # matches differences
+    r = np.random.default_rng(3)
+    x = r.standard_normal((1, 2, 7)); dt = r.uniform(-3, 1, (1, 2, 7)); A = -np.array([[1.0, 2.0], [0.5, 3.0]])
+    B = r.standard_normal((1, 2, 7)); C = r.standard_normal((1, 2, 7)); dy = r.standard_normal((1, 2, 7))
+    g = orc.scan_bwd(x, dt, A, B, C, dy)
+    assert not np.any(g["dz"]) and np.all(np.isfinite(g["dh0"]))
+    assert np.allclose(g["dD"], np.sum(dy * x, axis=(0, 2)), rtol=1e-13, atol=1e-13)
+    y0, _ = orc.scan(x, dt, A, B, C)
+    eps = 1e-6
+    xp = x.copy(); xp[0, 1, 3] += eps
+    xm = x.copy(); xm[0, 1, 3] -= eps
+    fd = (np.sum(dy * orc.scan(xp, dt, A, B, C)[0]) - np.sum(dy * orc.scan(xm, dt, A, B, C)[0])) / (2 * eps)
+    assert abs(fd - g["dx"][0, 1, 3]) < 1e-7
+
+
 def test_softplus_tails(orc):
     # Delta for very negative / positive logits: log1p(e^u) ~ e^u and ~ u + e^-u (no cancellation, no overflow).
     u = np.array([-40.0, -12.0, 0.0, 12.0, 40.0, 700.0])
@@ -88,6 +110,14 @@ MUTANTS = [
      "yr[t] = step(dstate, disc, use_softplus, xr[t > 0 ? t - 1 : 0]"),
     ("hfinal_zero", r"h_final\[ch \* dstate \+ n\] = h\[n\];", "h_final[ch * dstate + n] = 0.0;"),
     ("decode_bias_ignored", r"dt\[ch\], dt_bias \? dt_bias\[d\] : 0\.0", "dt[ch], 0.0"),
+    ("bwd_no_decay_term", r"dDelta \+= g\[n\] \* \(dcoef_dd \* Bv \* xv \+ hprev \* abar \* An\);",
+     "dDelta += g[n] * (dcoef_dd * Bv * xv);"),
+    ("bwd_no_skip_dx", r"double dDelta = 0\.0, dxv = ds \* Dv;", "double dDelta = 0.0, dxv = 0.0;"),
+    ("bwd_dC_uses_hprev", r"dC\[b \* N \* L \+ n \* L \+ t\] \+= ds \* hcur;", "dC[b * N * L + n * L + t] += ds * hprev;"),
+    ("bwd_adjoint_not_decayed", r"g\[n\] \*= abar;", "g[n] *= 1.0;"),
+    ("bwd_softplus_derivative", r"dDelta \* sigm\(u\)", "dDelta * sigm(-u)"),
+    ("bwd_silu_derivative", r"\(sg \* \(1\.0 \+ zv \* \(1\.0 - sg\)\)\)", "sg"),
+    ("bwd_zoh_dA_series", r"0\.5 \+ e \* \(1\.0 / 3\.0", "0.5 + e * (1.0 / 2.0"),
 ]
 
 
