@@ -16,7 +16,7 @@
  *
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE memory owned by the caller.  The library allocates nothing; the forward scan may
- *     need a caller-provided workspace (query its size first).
+ *     need, and the backward always needs, a caller-provided workspace (query its size first).
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default stream).  Buffers must stay
  *     alive until the stream has executed the call.  Nothing is synchronised implicitly.
  *   - Layouts are row-major with the sequence index innermost:  x, dt, z, y: [batch][dim][seqlen];
@@ -51,7 +51,7 @@ typedef enum {
   SSM_ERR_DTYPE = 3,        /* unknown io_dtype / y_dtype */
   SSM_ERR_UNSUPPORTED = 4,  /* unknown disc or dt_softplus value, negative segments */
   SSM_ERR_ALIGN = 5,        /* a pointer not aligned to its element size */
-  SSM_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ssm_scan_fwd_workspace_bytes() */
+  SSM_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ssm_scan_{fwd,bwd}_workspace_bytes() */
   SSM_ERR_HIP = 7           /* the HIP runtime refused a launch */
 } ssm_status;
 
@@ -101,6 +101,36 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt,
 ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* x, const void* dt,
                             const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
                             const void* z, void* y, void* stream);
+
+/* Bytes of device workspace ssm_scan_bwd needs for these parameters (always > 0 for valid parameters, 0 for invalid
+ * ones).  Pure host function. */
+size_t ssm_scan_bwd_workspace_bytes(const ssm_scan_params* p);
+
+/*
+ * Backward of ssm_scan_fwd: the gradients of a scalar loss given dL/dy and, optionally, dL/dh_final.  They are the
+ * chain rule through the operation above.  No state from the forward pass is needed: every intermediate state is
+ * recomputed from the inputs (Mamba paper, gitcode.csdn.net translation, section 3.3.2, the recomputation paragraph;
+ * alishangtian.com close reading, "hardware-aware algorithm", recomputation item).
+ *   Parameters as for ssm_scan_fwd, except: p->y_dtype is the dtype of dy and of the per-step gradients dx, ddt, dz;
+ *   p->segments is ignored (the backward always works in 64-step chunks).
+ *   Inputs (device, as given to ssm_scan_fwd): x, dt, dt_bias, A, B, C, Dskip, z, h0;
+ *     dy [batch][dim][seqlen] y_dtype;  dh_final [batch][dim][dstate] fp32 or NULL (= 0).
+ *   Outputs (device, overwritten, never accumulated into):
+ *     dx, ddt [batch][dim][seqlen] y_dtype (ddt is the gradient with respect to dt, through the softplus);
+ *     dz [batch][dim][seqlen] y_dtype: required when z is given, must be NULL when it is not;
+ *     dA [dim][dstate] fp32;  dB, dC [batch][dstate][seqlen] fp32 (summed over channels);
+ *     dDskip [dim], ddt_bias [dim], dh0 [batch][dim][dstate] fp32, each optional (NULL = not computed).  dDskip and
+ *     ddt_bias are the gradients at the given values, also when Dskip / dt_bias are NULL (i.e. at 0).
+ *   workspace: device buffer of at least ssm_scan_bwd_workspace_bytes(p) bytes, 4-byte aligned.
+ *   stream: hipStream_t or NULL.
+ * Outputs must not overlap the inputs or each other.  Deterministic: every sum over channels, steps and batch runs in
+ * a fixed order, so repeated calls give bit-identical results.
+ */
+ssm_status ssm_scan_bwd(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
+                        const void* B, const void* C, const float* Dskip, const void* z, const float* h0,
+                        const void* dy, const float* dh_final, void* dx, void* ddt, float* dA, float* dB, float* dC,
+                        float* dDskip, void* dz, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Static description of a status code. */
 const char* ssm_status_str(ssm_status s);

@@ -1,15 +1,16 @@
-"""MI355X-native S6 selective scan (Mamba's selective SSM forward pass and single-token decode).
+"""MI355X-native S6 selective scan (Mamba's selective SSM: forward pass, backward pass and single-token decode).
 
-``scan_fwd`` and ``state_update`` call the C ABI of libssm57.so (include/ssm_scan.h) on PyTorch device tensors;
-the arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded synthetic workloads.
+``scan_fwd``, ``scan_bwd`` and ``state_update`` call the C ABI of libssm57.so (include/ssm_scan.h) on PyTorch device
+tensors; the arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded synthetic workloads.
 """
 from __future__ import annotations
 
 from . import _abi
-from ._abi import EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_params, workspace_bytes, plan_segments
+from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_params, workspace_bytes, plan_segments,
+                   bwd_workspace_bytes)
 
-__all__ = ["scan_fwd", "state_update", "EULER_B", "ZOH", "SSMError", "Params", "make_params", "workspace_bytes",
-           "plan_segments", "io_code"]
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "EULER_B", "ZOH", "SSMError", "Params", "make_params",
+           "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
 def io_code(dtype) -> int:
@@ -94,6 +95,60 @@ def scan_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=Non
                            _stream_handle(stream, x.device))
     _abi.check(st)
     return y, h_final
+
+
+def scan_bwd(x, dt, A, B, C, dy, dt_bias=None, Dskip=None, z=None, h0=None, dh_final=None, *, disc=EULER_B,
+             softplus=True, want_dDskip=True, want_ddt_bias=True, want_dh0=True, workspace=None, out=None,
+             stream=None):
+    """Gradients of the scan given dy (b, D, L) and optionally dh_final (b, D, N) float32, recomputing every state.
+
+    Inputs as for ``scan_fwd``; dy's dtype (float32 or bfloat16) is also the dtype of dx, ddt, dz.  Returns a dict with
+    dx, ddt, dz (None without a gate), dA (D, N), dB, dC (b, N, L), dDskip, ddt_bias (D,), dh0 (b, D, N) -- float32
+    except the per-step three.  ``out`` may pass preallocated tensors under the same keys.
+    """
+    import torch
+    b, D, L = x.shape
+    N = A.shape[1]
+    io = io_code(x.dtype)
+    gdt = dy.dtype
+    dev = x.device
+    f32 = torch.float32
+    _expect("x", x, (b, D, L), x.dtype, dev, optional=False)
+    _expect("dt", dt, (b, D, L), x.dtype, dev, optional=False)
+    _expect("z", z, (b, D, L), x.dtype, dev)
+    _expect("B", B, (b, N, L), x.dtype, dev, optional=False)
+    _expect("C", C, (b, N, L), x.dtype, dev, optional=False)
+    _expect("A", A, (D, N), f32, dev, optional=False)
+    _expect("dt_bias", dt_bias, (D,), f32, dev)
+    _expect("Dskip", Dskip, (D,), f32, dev)
+    _expect("h0", h0, (b, D, N), f32, dev)
+    _expect("dy", dy, (b, D, L), gdt, dev, optional=False)
+    _expect("dh_final", dh_final, (b, D, N), f32, dev)
+    p = make_params(b, D, L, N, io, io_code(gdt), disc, softplus, 0)
+    o = dict(out or {})
+    shapes = {"dx": ((b, D, L), gdt), "ddt": ((b, D, L), gdt), "dz": ((b, D, L), gdt), "dA": ((D, N), f32),
+              "dB": ((b, N, L), f32), "dC": ((b, N, L), f32), "dDskip": ((D,), f32), "ddt_bias": ((D,), f32),
+              "dh0": ((b, D, N), f32)}
+    wanted = {"dx": True, "ddt": True, "dz": z is not None, "dA": True, "dB": True, "dC": True, "dDskip": want_dDskip,
+              "ddt_bias": want_ddt_bias, "dh0": want_dh0}
+    for k, (shp, dtp) in shapes.items():
+        if not wanted[k]:
+            o[k] = None
+        elif o.get(k) is None:
+            o[k] = torch.empty(shp, dtype=dtp, device=dev)
+        else:
+            _expect(k, o[k], shp, dtp, dev)
+    need = bwd_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _abi.scan_bwd_raw(p, _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C), _addr(Dskip),
+                           _addr(z), _addr(h0), _addr(dy), _addr(dh_final), _addr(o["dx"]), _addr(o["ddt"]),
+                           _addr(o["dA"]), _addr(o["dB"]), _addr(o["dC"]), _addr(o["dDskip"]), _addr(o["dz"]),
+                           _addr(o["ddt_bias"]), _addr(o["dh0"]), _addr(workspace), ws_bytes,
+                           _stream_handle(stream, dev))
+    _abi.check(st)
+    return o
 
 
 def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=None, y_dtype=None, disc=EULER_B,

@@ -16,7 +16,7 @@ EULER_B, ZOH = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_UNSUPPORTED",
           5: "SSM_ERR_ALIGN", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_HIP"}
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
-           "ssm_abi_version", "ssm_scan_fwd_plan_segments"]
+           "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd"]
 
 
 class Params(ctypes.Structure):
@@ -54,6 +54,10 @@ def lib():
         L.ssm_scan_fwd.restype = ctypes.c_int
         L.ssm_state_update.argtypes = [PP] + [P] * 11
         L.ssm_state_update.restype = ctypes.c_int
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [PP]
+        L.ssm_scan_bwd_workspace_bytes.restype = S
+        L.ssm_scan_bwd.argtypes = [PP] + [P] * 20 + [P, S, P]
+        L.ssm_scan_bwd.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -86,6 +90,17 @@ def scan_fwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, w
     """Direct call with integer device addresses (0 = NULL)."""
     return lib().ssm_scan_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
                               workspace_bytes_, stream)
+
+
+def bwd_workspace_bytes(p: Params) -> int:
+    return int(lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def scan_bwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, dy, dh_final, dx, ddt, dA, dB, dC, dDskip, dz,
+                 ddt_bias, dh0, workspace, workspace_bytes_, stream):
+    """Direct call with integer device addresses (0 = NULL)."""
+    return lib().ssm_scan_bwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, dy, dh_final, dx, ddt, dA, dB,
+                              dC, dDskip, dz, ddt_bias, dh0, workspace, workspace_bytes_, stream)
 
 
 def state_update_raw(p: Params, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):

@@ -4,25 +4,23 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "ssm_scan.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssm_scan.hip", "ssm_scan_bwd.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm57.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-shared", "-Wall",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
     # packed FP32 (v_pk_*_f32) stays off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + FLAGS + ["-I", INC, SRC, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,7 +29,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every translation unit (in parallel) and link libssm57.so."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tag = ".tmp%d" % os.getpid()
+    objs = [os.path.splitext(s)[0] + tag + ".o" for s in SRCS]
+    try:
+        with ThreadPoolExecutor(len(SRCS)) as ex:
+            list(ex.map(lambda so: _run([hipcc] + FLAGS + ["-I", INC, "-c", so[0], "-o", so[1]], verbose),
+                        zip(SRCS, objs)))
+        _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", LIB + tag], verbose)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    os.replace(LIB + tag, LIB)
     return LIB
 
 

@@ -22,20 +22,54 @@
 //    computes every segment's zero-start end state and sum of Delta, a tiny pass chains them into carry-in states
 //    (exp(A * sum Delta) is the product of the segment's decays), and the main pass rescans each segment from its
 //    carry-in.
-#include <hip/hip_runtime.h>
+#include "common.hpp"
 
-#include <cstdarg>
-#include <cstdint>
-#include <cstdio>
-#include <cstring>
-#include <utility>
 
-#include "ssm_scan.h"
+namespace ssm57 {
+
+thread_local char g_err[512] = "";
+
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ssm_status check_common(const ssm_scan_params* p, bool need_seqlen) {
+  if (!p) return fail(SSM_ERR_NULL, "params is NULL");
+  if (p->batch < 1 || p->dim < 1 || (need_seqlen && p->seqlen < 1))
+    return fail(SSM_ERR_SHAPE, "batch=%lld dim=%lld seqlen=%lld must be >= 1", (long long)p->batch,
+                (long long)p->dim, (long long)p->seqlen);
+  if (p->dstate < 1 || p->dstate > SSM57_MAX_DSTATE)
+    return fail(SSM_ERR_SHAPE, "dstate=%lld must be in [1, %d]", (long long)p->dstate, SSM57_MAX_DSTATE);
+  if (p->io_dtype != SSM_F32 && p->io_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown io_dtype %d", p->io_dtype);
+  if (p->y_dtype != SSM_F32 && p->y_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown y_dtype %d", p->y_dtype);
+  if (p->disc != SSM_DISC_EULER_B && p->disc != SSM_DISC_ZOH)
+    return fail(SSM_ERR_UNSUPPORTED, "unknown disc %d", p->disc);
+  if (p->dt_softplus != 0 && p->dt_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "dt_softplus must be 0 or 1 (got %d)", p->dt_softplus);
+  if (p->segments < 0) return fail(SSM_ERR_UNSUPPORTED, "segments must be >= 0 (got %d)", p->segments);
+  if (p->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved must be 0");
+  // index arithmetic is 64-bit; keep element counts well inside it and the grid inside HIP's limits
+  const double elems = static_cast<double>(p->batch) * static_cast<double>(p->dim) *
+                       static_cast<double>(need_seqlen ? p->seqlen : 1) * 1.0;
+  if (elems > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
+  if (p->batch > 65535) return fail(SSM_ERR_SHAPE, "batch=%lld exceeds 65535", (long long)p->batch);
+  if (need_seqlen && p->seqlen > kMaxSeqlen)
+    return fail(SSM_ERR_SHAPE, "seqlen=%lld exceeds %lld (per-lane 32-bit buffer offsets)", (long long)p->seqlen,
+                (long long)kMaxSeqlen);
+  if ((p->dim + 15) / 16 > 0x7fffffffLL) return fail(SSM_ERR_SHAPE, "dim too large");
+  return SSM_OK;
+}
+
+}  // namespace ssm57
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+using namespace ssm57;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kChanPerWG = 16;  // 16 rows of 16 lanes
@@ -44,139 +78,6 @@ constexpr int kSub = 16;        // steps per transposition block (= lanes per ro
 constexpr int kBStride = kChunk + 4;   // sB row stride (floats): conflict-free b128 column reads
 constexpr int kCtStride = kSub + 4;    // sCt/sH step stride (floats)
 constexpr int kHRow = kSub * kCtStride + 16;  // sH row stride: rows of one wave land on different banks
-// 16 rows x L x 4 bytes must stay below 2^31 (buffer offsets; larger offsets address the drop region)
-constexpr int64_t kMaxSeqlen = int64_t(1) << 25;
-
-// ---------------------------------------------------------------------------------------------------------------
-// element access
-
-template <typename T>
-struct Elem;
-template <>
-struct Elem<float> {
-  using Raw = float;
-  static __device__ __forceinline__ float cvt(Raw r) { return r; }
-  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
-  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
-};
-template <>
-struct Elem<uint16_t> {  // bf16 stored as its bit pattern
-  using Raw = uint16_t;
-  static __device__ __forceinline__ float cvt(Raw r) { return __uint_as_float(static_cast<uint32_t>(r) << 16); }
-  static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
-    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-  }
-  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
-    p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32: round to nearest even
-  }
-};
-
-// ---------------------------------------------------------------------------------------------------------------
-// buffer (resource-descriptor) access: one descriptor per workgroup and tensor, 32-bit byte offsets per lane.  A read
-// past num_records returns 0 and a write past it is dropped, so partial tiles need no clamping and cannot fault.
-
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords: the gfx9-family descriptor format
-constexpr uint32_t kDropOffset = 0x80000000u;  // >= every num_records used below: the access is out of range
-
-template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, int64_t elems) {
-  int64_t bytes = elems * static_cast<int64_t>(sizeof(T));
-  bytes = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           static_cast<int>(kRsrcWord3));
-}
-
-template <typename T>
-struct Buf;
-template <>
-struct Buf<float> {
-  using Raw = float;
-  static __device__ __forceinline__ Raw ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
-  }
-  static __device__ __forceinline__ float cvt(Raw v) { return v; }
-  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, static_cast<int>(off), 0, 0);
-  }
-};
-template <>
-struct Buf<uint16_t> {
-  using Raw = uint16_t;
-  static __device__ __forceinline__ Raw ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0));
-  }
-  static __device__ __forceinline__ float cvt(Raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, static_cast<__bf16>(v)), r, static_cast<int>(off),
-                                          0, 0);
-  }
-};
-
-// ---------------------------------------------------------------------------------------------------------------
-// scalar math (fp32).  exp2/log2/rcp are the hardware transcendental instructions.
-
-__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// log(1 + v) for v in [0, 1].  With w = fl(1 + v), the rounding error e = (w - 1) - v is exact (Sterbenz) and
-// log(1 + v) = log(w) - e / w + O(e^2).  |e| <= 2^-24, so 1/w may be replaced by (1 - v) (relative difference v^2):
-// log1p(v) = log(w) + (v - (w - 1)) * (1 - v), accurate to a few ulp with no division or branch (w == 1 gives v).
-__device__ __forceinline__ float log1p_01(float v) {
-  const float w = 1.0f + v;
-  const float c = v - (w - 1.0f);
-  return fmaf(c, 1.0f - v, hw_log2(w) * kLn2);
-}
-
-// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e^-|u|)   (tau_Delta of paper section 3.2)
-__device__ __forceinline__ float softplus(float u) {
-  float v = hw_exp2(-fabsf(u) * kLog2e);
-  return fmaxf(u, 0.0f) + log1p_01(v);
-}
-
-// silu(z) = z * sigmoid(z)   (gate of the Mamba block)
-__device__ __forceinline__ float silu(float z) { return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e)); }
-
-// expm1(e) given a = exp(e): Taylor polynomial near 0 (|e| < 1/4, truncation < 2e-10 relative), a - 1 elsewhere.
-__device__ __forceinline__ float expm1_from(float e, float a) {
-  float p = 1.0f / 5040.0f;
-  p = fmaf(p, e, 1.0f / 720.0f);
-  p = fmaf(p, e, 1.0f / 120.0f);
-  p = fmaf(p, e, 1.0f / 24.0f);
-  p = fmaf(p, e, 1.0f / 6.0f);
-  p = fmaf(p, e, 0.5f);
-  p = fmaf(p, e, 1.0f);
-  p = p * e;
-  return fabsf(e) < 0.25f ? p : a - 1.0f;
-}
-
-// broadcast lane K of each 16-lane row (DPP row_newbcast); folds into the consuming VALU instruction
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf,
-                                                               false));
-}
-
-template <typename F, int... Ks>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
-  (f(std::integral_constant<int, Ks>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// single-dword LDS write that the compiler cannot merge with its neighbours into a two-dword write
-template <int OFF>
-__device__ __forceinline__ void lds_write_b32(uint32_t lds_addr, float v) {
-  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(lds_addr), "v"(v), "i"(OFF) : "memory");
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 struct ScanArgs {
   const void* x;
@@ -553,47 +454,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 
 // ---------------------------------------------------------------------------------------------------------------
 // host side: validation, planning, dispatch
-
-thread_local char g_err[512] = "";
-
-ssm_status fail(ssm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-ssm_status fail(ssm_status s, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
-  va_end(ap);
-  return s;
-}
-
-bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
-
-ssm_status check_common(const ssm_scan_params* p, bool need_seqlen) {
-  if (!p) return fail(SSM_ERR_NULL, "params is NULL");
-  if (p->batch < 1 || p->dim < 1 || (need_seqlen && p->seqlen < 1))
-    return fail(SSM_ERR_SHAPE, "batch=%lld dim=%lld seqlen=%lld must be >= 1", (long long)p->batch,
-                (long long)p->dim, (long long)p->seqlen);
-  if (p->dstate < 1 || p->dstate > SSM57_MAX_DSTATE)
-    return fail(SSM_ERR_SHAPE, "dstate=%lld must be in [1, %d]", (long long)p->dstate, SSM57_MAX_DSTATE);
-  if (p->io_dtype != SSM_F32 && p->io_dtype != SSM_BF16)
-    return fail(SSM_ERR_DTYPE, "unknown io_dtype %d", p->io_dtype);
-  if (p->y_dtype != SSM_F32 && p->y_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown y_dtype %d", p->y_dtype);
-  if (p->disc != SSM_DISC_EULER_B && p->disc != SSM_DISC_ZOH)
-    return fail(SSM_ERR_UNSUPPORTED, "unknown disc %d", p->disc);
-  if (p->dt_softplus != 0 && p->dt_softplus != 1)
-    return fail(SSM_ERR_UNSUPPORTED, "dt_softplus must be 0 or 1 (got %d)", p->dt_softplus);
-  if (p->segments < 0) return fail(SSM_ERR_UNSUPPORTED, "segments must be >= 0 (got %d)", p->segments);
-  if (p->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved must be 0");
-  // index arithmetic is 64-bit; keep element counts well inside it and the grid inside HIP's limits
-  const double elems = static_cast<double>(p->batch) * static_cast<double>(p->dim) *
-                       static_cast<double>(need_seqlen ? p->seqlen : 1) * 1.0;
-  if (elems > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
-  if (p->batch > 65535) return fail(SSM_ERR_SHAPE, "batch=%lld exceeds 65535", (long long)p->batch);
-  if (need_seqlen && p->seqlen > kMaxSeqlen)
-    return fail(SSM_ERR_SHAPE, "seqlen=%lld exceeds %lld (per-lane 32-bit buffer offsets)", (long long)p->seqlen,
-                (long long)kMaxSeqlen);
-  if ((p->dim + 15) / 16 > 0x7fffffffLL) return fail(SSM_ERR_SHAPE, "dim too large");
-  return SSM_OK;
-}
 
 struct Plan {
   int nseg;

@@ -12,7 +12,8 @@ softplus^-1 of a value log-uniform in a range around [0.001, 0.1].
 Recipe (also written out in the design doc):
   * every tensor k of workload `cfg` at decode step `step` is drawn in flattened chunks of 2**24 elements, chunk i
     from numpy's default_rng(SeedSequence(57, spawn_key=(cfg, step, k, i)));
-  * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state;
+  * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state, 9 dy, 10 dh_final
+    (the last two are the cotangents fed to the backward pass);
   * normals are numpy float32 standard normals; log-uniforms are exp(uniform(log lo, log hi)) in float64;
   * Delta-logit = softplus^-1(Delta*) - bias[d], with softplus^-1(v) = log(expm1(v)), rounded to the io dtype;
   * bf16 values are rounded to nearest-even from float32 (float64 -> float32 -> bf16 for float64 sources).
@@ -218,6 +219,22 @@ def scan_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
     if with_h0:
         out["h0"] = _normal(c, 0, 8, b * D * N).reshape(b, D, N)
     return out
+
+
+def cotangents(w: Workload, step: int = 0, io: str | None = None, with_dh_final: bool = False) -> dict:
+    """Cotangents for the backward pass: dy (b, D, L) N(0, 1) in storage dtype `io` (default: the workload's) and,
+    optionally, dh_final (b, D, N) f32 N(0, 1)."""
+    b, D, N, L = w.batch, w.dim, w.dstate, w.seqlen
+    c = w.cfg_id
+    dy = _normal_storage(c, step, 9, b * D * L, io or w.io).reshape(b, D, L)
+    dhf = _normal(c, step, 10, b * D * N).reshape(b, D, N) if with_dh_final else None
+    return {"dy": dy, "dh_final": dhf}
+
+
+def random_small_cotangents(seed: int, b: int, D: int, L: int, N: int, io: str = F32, dh_final=False) -> dict:
+    """Cotangents matching random_small(seed, ...)."""
+    w = Workload("small", b, D, L, N, io, 1e-3, 1e-1, 0.0, cfg_id=1000 + seed)
+    return cotangents(w, io=io, with_dh_final=dh_final)
 
 
 def decode_state(w: Workload) -> np.ndarray:
