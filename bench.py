@@ -5,8 +5,10 @@
 A step is one forward scan (softplus Delta, discretisation, recurrence, C-contraction, D skip, SiLU gate, final
 state: one fused launch) over the Mamba-2.8B-layer-shaped workload: batch 4, d_inner 5120, L 4096, N 16, bf16 I/O,
 fp32 state, seeded synthetic inputs already resident in HBM.  Prints one JSON line.  Also reported, outside `value`:
-the single-token decode step (batch 256, d_inner 5120, 64 steps with fresh inputs) and the fp64 CPU oracle timed
-on the host cores over the same step (it is a reported baseline; its output also gates parity of the timed step).
+the backward pass over the same workload (one ssm_scan_bwd call: every gradient, states recomputed, bf16 dy and
+per-step gradients), the single-token decode step (batch 256, d_inner 5120, 64 steps with fresh inputs) and the fp64
+CPU oracle timed on the host cores over the same step (a reported baseline; its output also gates parity of the timed
+step).
 """
 from __future__ import annotations
 
@@ -42,15 +44,38 @@ def scan_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
     return 2.0 * per_elem * b * D * L
 
 
+def bwd_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
+    """fp32 work of the backward per (b, d, t), in FMA-slot units x 2 FLOP (same convention as the forward).
+    Per state n: zero-start chunk pass 8 (Delta*A, exp 2, (Delta x)*B, h FMA, decay product, C*ds, lambda FMA);
+    recomputation 5 (Delta*A, exp 2, (Delta x)*B, h FMA); adjoint 2 (g += C ds, g *= a); dA 3 (a h_prev, g u,
+    += Delta); dx / dDelta terms 2 (g B, A g u) and their sums over n 2; dB / dC 2 FMA; with the gate C h and its sum 2.
+    Per element: softplus twice (11 each), sigmoid(u) 4, silu twice (7 each), dz 4, dx / dDelta / du 4."""
+    per_n = 8 + 5 + 2 + 3 + 4 + 2 + (2 if gate else 0)
+    per_elem = 11 * 2 + 4 + (7 * 2 + 4 if gate else 0) + 4 + (2 if dskip else 0)
+    return 2.0 * (per_n * N + per_elem) * b * D * L
+
+
+def bwd_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
+    """Inputs read twice (x, dt, z, dy by the chunk pass and the main pass), B and C twice, per-step gradients
+    written once, dB / dC / dA / dD / dbias / dh0 written once (fp32)."""
+    seq_in = b * D * L * io_bytes * (3 + (1 if gate else 0))
+    seq_out = b * D * L * io_bytes * (2 + (1 if gate else 0))
+    bc = 2 * b * N * L * io_bytes
+    return 2 * seq_in + seq_out + 2 * bc + 2 * b * N * L * 4 + D * N * 4 * 2 + D * 4 * 4 + b * D * N * 4
+
+
 def decode_algorithmic_bytes(b, D, N, io_bytes=2, gate=True, dskip=True):
     return (b * D * N * 4 * 2 + b * D * io_bytes * (3 + (1 if gate else 0)) + 2 * b * N * io_bytes + D * N * 4
             + D * 4 * (2 if dskip else 1))
 
 
 def src_hash():
+    """Hash of every kernel source file: counter records taken on other sources are stale."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "selective_state_space_57_amd", "csrc", "ssm_scan.hip"), "rb") as f:
-        h.update(f.read())
+    csrc = os.path.join(ROOT, "selective_state_space_57_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -88,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (torch) five times: the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -180,6 +207,51 @@ def main():
                      "kernel": kernel_key, "algorithmic_flops": flops},
         "host_wall_ms_timed_region": wall_ms,
     }
+
+    # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
+    if not args.no_bwd:
+        from selective_state_space_57_amd import _abi
+        dy = up(I.cotangents(w)["dy"])
+        pb = ssm.make_params(b, D, L, N, ssm.SSM_BF16, ssm.SSM_BF16)
+        wsb_n = ssm.bwd_workspace_bytes(pb)
+        wsb = torch.empty(wsb_n, dtype=torch.uint8, device=dev)
+        bf, f32 = torch.bfloat16, torch.float32
+        g = {"dx": torch.empty((b, D, L), dtype=bf, device=dev), "ddt": torch.empty((b, D, L), dtype=bf, device=dev),
+             "dz": torch.empty((b, D, L), dtype=bf, device=dev), "dA": torch.empty((D, N), dtype=f32, device=dev),
+             "dB": torch.empty((b, N, L), dtype=f32, device=dev), "dC": torch.empty((b, N, L), dtype=f32, device=dev),
+             "dD": torch.empty((D,), dtype=f32, device=dev), "db": torch.empty((D,), dtype=f32, device=dev),
+             "dh0": torch.empty((b, D, N), dtype=f32, device=dev)}
+        bargs = (d["x"].data_ptr(), d["dt"].data_ptr(), d["dt_bias"].data_ptr(), d["A"].data_ptr(),
+                 d["B"].data_ptr(), d["C"].data_ptr(), d["Dskip"].data_ptr(), d["z"].data_ptr(), 0, dy.data_ptr(), 0,
+                 g["dx"].data_ptr(), g["ddt"].data_ptr(), g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(),
+                 g["dD"].data_ptr(), g["dz"].data_ptr(), g["db"].data_ptr(), g["dh0"].data_ptr(), wsb.data_ptr(),
+                 wsb_n, stream.cuda_stream)
+
+        def bstep():
+            st = _abi.scan_bwd_raw(pb, *bargs)
+            if st:
+                _abi.check(st)
+
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.bwd_steps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.bwd_steps
+        bfl = bwd_algorithmic_flops(b, D, L, N)
+        bby = bwd_algorithmic_bytes(b, D, L, N)
+        out["bwd"] = {"workload": "mamba2.8b-layer", "steps": args.bwd_steps, "ms_per_step": bms,
+                      "elements_per_s": elems / (bms * 1e-3), "ratio_to_forward": bms / ms,
+                      "kernels": "prep + carry + main + 2 reduce (one ssm_scan_bwd call)",
+                      "algorithmic_flops": bfl, "achieved_TFLOPs": bfl / (bms * 1e-3) / 1e12,
+                      "frac_of_valu_peak": bfl / (bms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS,
+                      "algorithmic_bytes": bby, "achieved_GBps": bby / (bms * 1e-3) / 1e9,
+                      "workspace_bytes": wsb_n}
+        del wsb
 
     # ---- decode: 64 single-token steps with fresh inputs (batch 256, d_inner 5120)
     if not args.no_decode:

@@ -21,19 +21,19 @@
 //    No atomics anywhere: results are bit-identical from run to run.
 //  * Lane layout as in the forward: one lane per (channel, state n), a 16-lane DPP row per channel, per-step Delta,
 //    Delta*x and ds broadcast from their owner lane with row_newbcast.
-//  * Sums over n (dx, dDelta and, with the gate, the pre-gate output for dz) go through a per-wave LDS transposition:
-//    each lane writes its per-step terms, lane j of the row reads the 16 terms of step j and adds them.
-//  * Sums over channels (dB_n(t) = sum_d g Delta x, dC_n(t) = sum_d ds h) run on the matrix cores: one
-//    v_mfma_f32_16x16x4_f32 per step contracts the 4 channels of a wave (K = 4 = the wave's rows) with a one-hot
-//    operand that routes the product into column t of a 16 (n) x 16 (t) accumulator tile.  The tiles accumulate over
-//    every channel quad the wave visits, so a workgroup hands in one partial per (n, t) however many channels it owns.
+//  * Per 16-step block every lane writes its adjoint g, a dDelta term and its state to a per-wave LDS transposition;
+//    lane j of each row then owns step j of its channel and reads the 16 states' values of that step.  It forms the
+//    sums over n (dx, dDelta and, with the gate, the pre-gate output for dz) and the per-channel products of
+//    dB_n(t) = sum_d g Delta x and dC_n(t) = sum_d ds h, which it reduces over the wave's 4 channels with two rounds of
+//    gfx950's v_permlane32_swap / v_permlane16_swap: after them each row holds a different quarter (B or C, 8 states)
+//    of the 4-channel sums for its step.  These accumulate in registers over every channel quad the wave visits, so a
+//    workgroup hands in one partial per (n, t) however many channels it owns.  (An fp32 MFMA per step can do the same
+//    contraction over the 4 rows, but 16x16x4 MFMAs with one useful column cost more than the VALU they save.)
 #include "common.hpp"
 
 namespace {
 
 using namespace ssm57;
-
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBT = 64;              // steps per chunk
 constexpr int kBlk = 16;             // steps per block (= lanes per row)
@@ -41,6 +41,7 @@ constexpr int kNB = kBT / kBlk;      // blocks per chunk
 constexpr int kSlots = kNB + 1;      // per (channel, chunk): local states after blocks 0..kNB-2, end state, lambda
 constexpr int kNP = 16;              // state axis padded to 16 in workspace arrays
 constexpr int kSStride = kBT + 4;    // sB / sC row stride (floats): conflict-free b128 reads along t
+constexpr int kTStride = kNP + 4;    // sBt / sCt ([t][n] copies) step stride: conflict-free b128 reads along n
 constexpr int kTS = 3 * kBlk + 4;    // transposition: floats per step (3 terms x 16 states + pad; 52/4 is odd)
 constexpr int kTR = kBlk * kTS + 16; // transposition: floats per row (rows of a wave on different bank groups)
 constexpr int kTW = 4 * kTR;         // transposition: floats per wave
@@ -81,7 +82,8 @@ __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2
 // B and C of one chunk into LDS as fp32, [n][t]; zero outside the sequence and the state range
 template <typename TI>
 __device__ __forceinline__ void stage_bc(float (*sB)[kSStride], float (*sC)[kSStride], const BwdArgs& p, int64_t b,
-                                         int t0, int tid) {
+                                         int t0, int tid, float (*sBt)[kTStride] = nullptr,
+                                         float (*sCt)[kTStride] = nullptr) {
   const int nn = tid >> 4, t4 = (tid & 15) * 4;
   float bv[4], cv[4];
 #pragma unroll
@@ -94,6 +96,25 @@ __device__ __forceinline__ void stage_bc(float (*sB)[kSStride], float (*sC)[kSSt
   }
   *reinterpret_cast<float4*>(&sB[nn][t4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
   *reinterpret_cast<float4*>(&sC[nn][t4]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+  if (sBt) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sBt[t4 + k][nn] = bv[k];
+      sCt[t4 + k][nn] = cv[k];
+    }
+  }
+}
+
+// x + y after swapping the upper 32 lanes of x with the lower 32 lanes of y: lanes 0..31 get x(l) + x(l + 32),
+// lanes 32..63 get y(l - 32) + y(l)
+__device__ __forceinline__ float swap32_add(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// the same within 32-lane halves: even 16-lane rows get x(row) + x(row + 1), odd rows y(row - 1) + y(row)
+__device__ __forceinline__ float swap16_add(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // An integer the compiler cannot see through.  B / C in LDS are the same for every channel quad a wave visits; left
@@ -104,11 +125,22 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// s broadcast from lane K of the row, times v, as one v_mul_f32_dpp.  Written out because the compiler may commute a
+// plain product so that the broadcast lands in the second operand, where DPP cannot apply, and then spends a
+// separate v_mov_b32_dpp on it.
+template <int K>
+__device__ __forceinline__ float mul_bcast(float s, float v) {
+  float r;
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=v"(r)
+      : "v"(s), "v"(v), "i"(K));
+  return r;
+}
+
 // Anchors a running value in a register at this point.  Accumulators that are read only after the last block (lambda,
 // dA, the MFMA tiles, ...) would otherwise have their whole update chains sunk to that read, keeping every block's
 // decays and operands live at once.
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void pin(v4f& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ void read16(const float* src, float out[kBlk]) {
 #pragma unroll
@@ -231,9 +263,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
       const float uv = cvt<TI>(cur.dt) + bias;
       float delta = p.softplus ? softplus(uv) : uv;
       delta = ev ? delta : 0.0f;
-      const float dxo = delta * xv;
+      float dxo = delta * xv;
       const float dyv = cvt<TG>(cur.dy);
-      const float ds = GATE ? dyv * silu(cvt<TI>(cur.z)) : dyv;
+      float ds = GATE ? dyv * silu(cvt<TI>(cur.z)) : dyv;
+      float xb = xv;
+      // anchor this block's per-step values here: their row broadcasts must not be hoisted into earlier blocks,
+      // where they could no longer fold into the multiplies that consume them
+      pin(delta);
+      pin(dxo);
+      pin(ds);
+      pin(xb);
       float bq[kBlk], cq[kBlk];
       read16(&sB[0][0] + boff + I * kBlk, bq);
       read16(&sC[0][0] + boff + I * kBlk, cq);
@@ -244,13 +283,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
         float bb;
         if constexpr (ZOH) {
           const float coef = An != 0.0f ? expm1_from(dk * An, a) * rA : dk;
-          bb = coef * bq[K] * row_bcast<K>(xv);
+          bb = coef * bq[K] * row_bcast<K>(xb);
         } else {
           bb = row_bcast<K>(dxo) * bq[K];
         }
         h = fmaf(a, h, bb);
         E *= a;
-        lam = fmaf(E, row_bcast<K>(ds) * cq[K], lam);
+        lam = fmaf(E, mul_bcast<K>(ds, cq[K]), lam);
       });
       float s = delta;
       s += __shfl_xor(s, 8, 16);
@@ -320,7 +359,9 @@ template <typename TI, typename TG, bool ZOH, bool GATE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_main_kernel(BwdArgs p) {
   __shared__ __align__(16) float sB[kNP][kSStride];
   __shared__ __align__(16) float sC[kNP][kSStride];
-  __shared__ __align__(16) float sT[4 * kTW];  // per-wave transposition buffers, then the tile reduction
+  __shared__ __align__(16) float sBt[kBT][kTStride];  // B, C again as [t][n] for the step owners
+  __shared__ __align__(16) float sCt[kBT][kTStride];
+  __shared__ __align__(16) float sT[4 * kTW];  // per-wave transposition buffers, then the partial reduction
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so per-quad descriptors are SGPRs
   const int n = lane & 15, r = lane >> 4;
@@ -330,19 +371,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int t0 = k * kBT;
   const bool nv = n < p.N;
 
-  stage_bc<TI>(sB, sC, p, b, t0, tid);
+  stage_bc<TI>(sB, sC, p, b, t0, tid, sBt, sCt);
   __syncthreads();
 
   float* const tw = &sT[w * kTW];
   const uint32_t tw_wr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tw + r * kTR + n));
   const float* const tw_rd = tw + r * kTR + n * kTS;
 
-  v4f tB[kNB], tC[kNB];  // dB / dC tiles: lane l, element c holds (n = 4 (l / 16) + c, t = 16 i + l % 16)
+  // 4-channel sums of dB (rows 0, 1) / dC (rows 2, 3) for states 8 (r % 2) + m at step t0 + 16 i + n, summed over
+  // the quads this wave visits
+  float acc[kNB][8];
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) {
-    tB[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    tC[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int i = 0; i < kNB; ++i)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[i][m] = 0.0f;
 
   auto quad0 = [&](int q) { return (static_cast<int64_t>(g) * p.Q + q) * 16 + w * 4; };  // first channel of a quad
   auto chan = [&](int q) { return quad0(q) + r; };
@@ -410,11 +452,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       const float uv = cvt<TI>(cur.dt) + bias;
       float delta = p.softplus ? softplus(uv) : uv;
       delta = ev ? delta : 0.0f;  // padded steps are the identity
-      const float dxo = delta * xv;
+      float dxo = delta * xv;
       const float dyv = cvt<TG>(cur.dy);
       const float zv = GATE ? cvt<TI>(cur.z) : 0.0f;
       const float sz = GATE ? sigmoid(zv) : 0.0f;
-      const float ds = GATE ? dyv * zv * sz : dyv;
+      float ds = GATE ? dyv * zv * sz : dyv;
+      float xb = xv;
+      // anchor the per-step values (see prep): their broadcasts stay in this block and fold into the multiplies
+      pin(delta);
+      pin(dxo);
+      pin(ds);
+      pin(xb);
 
       // state entering the block
       float hb = sd.hin;
@@ -432,7 +480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         if constexpr (ZOH) {
           const float coef = An != 0.0f ? expm1_from(dk * An, a) * rA : dk;
           Cf[K] = coef;
-          bb = coef * bq[K] * row_bcast<K>(xv);
+          bb = coef * bq[K] * row_bcast<K>(xb);
         } else {
           bb = row_bcast<K>(dxo) * bq[K];
         }
@@ -447,16 +495,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       wave_lds_sync();  // the previous block's gathers of this wave are done
       static_for<kBlk>([&](auto kc) {
         constexpr int K = kBlk - 1 - decltype(kc)::value;
-        gam = fmaf(row_bcast<K>(ds), cq[K], gam);  // g_t = C_t ds_t + a_{t+1} g_{t+1}
+        // broadcast operands go through a multiply, where DPP folds into the instruction (an accumulate would not)
+        gam += mul_bcast<K>(ds, cq[K]);  // g_t = C_t ds_t + a_{t+1} g_{t+1}
         const float hp = K > 0 ? H[K > 0 ? K - 1 : 0] : hb;
         const float u = Aa[K] * hp;  // a_t h_{t-1}
-        const float dk = row_bcast<K>(delta);
-        float U, W;
+        float G, W;
         if constexpr (ZOH) {
-          const float gc = gam * Cf[K];
-          tB[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(gc, n == K ? xv : 0.0f, tB[I], 0, 0, 0);
-          U = gc * bq[K];                                  // dx term
-          const float bx = bq[K] * row_bcast<K>(xv);
+          const float dk = row_bcast<K>(delta);
+          G = gam * Cf[K];                                 // g coef: times B -> dx, times x -> dB
+          const float bx = row_bcast<K>(xb) * bq[K];
           W = gam * fmaf(An, u, Aa[K] * bx);               // dDelta term: g (a B x + A a h_{t-1})
           const float e = dk * An;                         // d coef / dA = Delta^2 sum_j (j+1) e^j / (j+2)!
           float s = 1.0f / 45360.0f;
@@ -471,32 +518,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
           dA_acc = fmaf(gam, fmaf(dcdA, bx, u * dk), dA_acc);
         } else {
           const float wv = gam * u;
-          dA_acc = fmaf(wv, dk, dA_acc);                   // dA: g Delta a h_{t-1}
-          tB[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(gam, n == K ? dxo : 0.0f, tB[I], 0, 0, 0);
-          U = gam * bq[K];                                 // times Delta -> dx, times x -> dDelta
+          dA_acc += mul_bcast<K>(delta, wv);              // dA: g Delta a h_{t-1}
+          G = gam;                                         // times B -> dx / dDelta, times Delta x -> dB
           W = An * wv;                                     // dDelta term A a h_{t-1} g
         }
-        tC[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(H[K], n == K ? ds : 0.0f, tC[I], 0, 0, 0);
-        lds_write_b32<(K * kTS) * 4>(tw_wr, U);
+        lds_write_b32<(K * kTS) * 4>(tw_wr, G);
         lds_write_b32<(K * kTS + kBlk) * 4>(tw_wr, W);
-        if constexpr (GATE) lds_write_b32<(K * kTS + 2 * kBlk) * 4>(tw_wr, cq[K] * H[K]);
+        lds_write_b32<(K * kTS + 2 * kBlk) * 4>(tw_wr, H[K]);
         gam *= Aa[K];
       });
       wave_lds_sync();
 
-      // lane n of the row: sums over the 16 states of step t
-      float SU = 0.0f, SW = 0.0f, SP = 0.0f;
+      // lane n of the row owns step t: sums over the 16 states, and the products for dB / dC reduced over the 4 rows
+      const float wB = ZOH ? xb : dxo;  // dB_n(t) gets G x (ZOH, G = g coef) or G Delta x (Euler, G = g)
+      float SU = 0.0f, SW = 0.0f, SP = 0.0f, v[kNP];
 #pragma unroll
-      for (int m = 0; m < kBlk / 4; ++m) {
-        const float4 u4 = *reinterpret_cast<const float4*>(tw_rd + 4 * m);
+      for (int m = 0; m < kNP / 4; ++m) {
+        const float4 g4 = *reinterpret_cast<const float4*>(tw_rd + 4 * m);
         const float4 w4 = *reinterpret_cast<const float4*>(tw_rd + kBlk + 4 * m);
-        SU += (u4.x + u4.y) + (u4.z + u4.w);
+        const float4 h4 = *reinterpret_cast<const float4*>(tw_rd + 2 * kBlk + 4 * m);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sBt[I * kBlk + n][4 * m]);
+        const float g[4] = {g4.x, g4.y, g4.z, g4.w}, hh[4] = {h4.x, h4.y, h4.z, h4.w};
+        SU = fmaf(g4.x, b4.x, SU);
+        SU = fmaf(g4.y, b4.y, SU);
+        SU = fmaf(g4.z, b4.z, SU);
+        SU = fmaf(g4.w, b4.w, SU);
         SW += (w4.x + w4.y) + (w4.z + w4.w);
         if constexpr (GATE) {
-          const float4 p4 = *reinterpret_cast<const float4*>(tw_rd + 2 * kBlk + 4 * m);
-          SP += (p4.x + p4.y) + (p4.z + p4.w);
+          const float4 c4 = *reinterpret_cast<const float4*>(&sCt[I * kBlk + n][4 * m]);
+          SP = fmaf(c4.x, h4.x, SP);
+          SP = fmaf(c4.y, h4.y, SP);
+          SP = fmaf(c4.z, h4.z, SP);
+          SP = fmaf(c4.w, h4.w, SP);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * m + i] = swap32_add(g[i] * wB, hh[i] * ds);  // rows 0,1: B; rows 2,3: C
       }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[I][m] += swap16_add(v[m], v[m + 8]);  // even rows: n < 8; odd rows: n >= 8
       float dxv, dD;
       if constexpr (ZOH) {
         dxv = fmaf(ds, Dv, SU);
@@ -522,8 +581,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       pin(dA_acc);
       pin(db_acc);
       pin(dD_acc);
-      pin(tB[I]);
-      pin(tC[I]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) pin(acc[I][m]);
     });
 
     const int64_t pk = (b * p.nck + k) * p.dim + d;
@@ -542,25 +601,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
   }
 
-  // sum the four waves' tiles and store the workgroup's dB / dC partial for this chunk
+  // sum the four waves' partials and store the workgroup's dB / dC partial for this chunk
   __syncthreads();
-  float* const tr = &sT[w * (2 * kNB * 4 * 64)];
+  constexpr int kPart = kNB * 8 * 64;  // floats per wave
+  float* const tr = &sT[w * kPart];
 #pragma unroll
   for (int i = 0; i < kNB; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      tr[((0 * kNB + i) * 4 + c) * 64 + lane] = tB[i][c];
-      tr[((1 * kNB + i) * 4 + c) * 64 + lane] = tC[i][c];
-    }
+    for (int m = 0; m < 8; ++m) tr[(i * 8 + m) * 64 + lane] = acc[i][m];
   __syncthreads();
-  constexpr int kTile = 2 * kNB * 4 * 64;
 #pragma unroll
-  for (int e = 0; e < kTile / 256; ++e) {
+  for (int e = 0; e < kPart / 256; ++e) {
     const int pos = e * 256 + tid;
-    const float v = (sT[pos] + sT[kTile + pos]) + (sT[2 * kTile + pos] + sT[3 * kTile + pos]);
+    const float v = (sT[pos] + sT[kPart + pos]) + (sT[2 * kPart + pos] + sT[3 * kPart + pos]);
     const int j = pos >> 6, l = pos & 63;
-    const int c = j & 3, i = (j >> 2) % kNB, qty = j / (4 * kNB);
-    const int nn = 4 * (l >> 4) + c;
+    const int i = j >> 3, m = j & 7, rr = l >> 4;
+    const int qty = rr >> 1, nn = 8 * (rr & 1) + m;
     const int64_t tt = t0 + i * kBlk + (l & 15);
     p.partBC[((((static_cast<int64_t>(g) * p.batch + b) * 2 + qty) * kNP + nn) * p.Lpad) + tt] = v;
   }
@@ -584,22 +640,41 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs p) {
   (qty ? p.dC : p.dB)[(b * p.N + nn) * p.L + t] = s;
 }
 
+// per-channel parameter gradients: out[o] = sum over the batch*nck partial rows of the partial at o.  A workgroup owns
+// 64 consecutive outputs; its four waves each sum a quarter of the rows (coalesced 256-byte rows, eight loads in
+// flight), and the quarters are added in a fixed order.  dA's outputs are (d, n) with n padded to 16; dD and
+// d dt_bias are (d, 0 / 1) of a second partial array with 2 per channel.
 __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs p) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= p.dim * (kNP + 2)) return;
-  const int64_t d = i / (kNP + 2);
-  const int j = static_cast<int>(i % (kNP + 2));
-  const int64_t terms = p.batch * p.nck;
-  float s = 0.0f;
-  if (j < kNP) {
-    if (j >= p.N) return;
-    for (int64_t m = 0; m < terms; ++m) s += p.partA[(m * p.dim + d) * kNP + j];
-    p.dA[d * p.N + j] = s;
+  __shared__ float part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t nA = p.dim * kNP, nP = p.dim * 2;
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * 64 + lane;  // flat output over [dA (dim*16) | dD,dbias (dim*2)]
+  const bool isA = o < nA;
+  const bool ok = o < nA + nP;
+  const float* src = isA ? p.partA + o : p.partP + (o - nA);
+  const int64_t stride = isA ? nA : nP;
+  const int64_t rows = p.batch * p.nck;
+  const int64_t r0 = rows * w / 4, r1 = rows * (w + 1) / 4;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t m = r0;
+  if (ok) {
+    for (; m + 8 <= r1; m += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += src[(m + u) * stride];
+    for (; m < r1; ++m) acc[0] += src[m * stride];
+  }
+  part[w][lane] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (w != 0 || !ok) return;
+  const float s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+  if (isA) {
+    const int64_t d = o / kNP;
+    const int n = static_cast<int>(o % kNP);
+    if (n < p.N) p.dA[d * p.N + n] = s;
   } else {
-    float* out = j == kNP ? p.dD : p.dbias;
-    if (!out) return;
-    for (int64_t m = 0; m < terms; ++m) s += p.partP[(m * p.dim + d) * 2 + (j - kNP)];
-    out[d] = s;
+    const int64_t d = (o - nA) / 2;
+    float* out = ((o - nA) & 1) ? p.dbias : p.dD;
+    if (out) out[d] = s;
   }
 }
 
@@ -726,8 +801,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_params* p, const void* x, const void* dt,
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
-    const int64_t nthr = p->dim * (kNP + 2);
-    hipLaunchKernelGGL(bwd_reduce_par_kernel, dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0, st, a);
+    const int64_t nout = p->dim * (kNP + 2);
+    hipLaunchKernelGGL(bwd_reduce_par_kernel, dim3(static_cast<unsigned>((nout + 63) / 64)), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
