@@ -250,7 +250,8 @@ def main():
                       "algorithmic_flops": bfl, "achieved_TFLOPs": bfl / (bms * 1e-3) / 1e12,
                       "frac_of_valu_peak": bfl / (bms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS,
                       "algorithmic_bytes": bby, "achieved_GBps": bby / (bms * 1e-3) / 1e9,
-                      "workspace_bytes": wsb_n}
+                      "workspace_bytes": wsb_n,
+                      "main_kernel_traffic": measured_traffic("bwd_main_kernel<bf16,bf16,euler,gate> mamba2.8b-layer")}
         del wsb
 
     # ---- decode: 64 single-token steps with fresh inputs (batch 256, d_inner 5120)

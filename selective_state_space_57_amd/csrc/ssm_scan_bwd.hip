@@ -315,6 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 // rho(last) = dh_final, rho(k-1) = P_k rho(k) + lambda_k, written over lambda_k; dh0 = P_0 rho(0) + lambda_0.
 
 __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
+  constexpr int U = 8;  // chunks whose loads are in flight together; the dependent chain is two FMAs per chunk
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t bd = i >> 4;
   const int n = static_cast<int>(i & 15);
@@ -323,31 +324,36 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
   const float Ap = p.A[d * p.N + n] * kLog2e;
   float* const sp = p.side + bd * p.nck * (kSlots * kNP) + n;
   const float* const cp = p.cum + bd * p.nck * kNB + (kNB - 1);
+  auto slot = [&](int k, int j) { return sp + static_cast<int64_t>(k) * (kSlots * kNP) + j * kNP; };
   float hs = p.h0 ? p.h0[bd * p.N + n] : 0.0f;
-  float e_next = sp[(kNB - 1) * kNP];
-  float tot_next = cp[0];
-  for (int k = 0; k < p.nck; ++k) {
-    float* const s = sp + static_cast<int64_t>(k) * (kSlots * kNP) + (kNB - 1) * kNP;
-    const float e = e_next, tot = tot_next;
-    if (k + 1 < p.nck) {  // load ahead of the dependent chain
-      e_next = s[kSlots * kNP];
-      tot_next = cp[static_cast<int64_t>(k + 1) * kNB];
+  for (int k0 = 0; k0 < p.nck; k0 += U) {
+    float e[U], P[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = k0 + u < p.nck;
+      e[u] = ok ? *slot(k0 + u, kNB - 1) : 0.0f;
+      P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k0 + u) * kNB] * Ap) : 1.0f;
     }
-    *s = hs;
-    hs = fmaf(hw_exp2(tot * Ap), hs, e);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < p.nck) *slot(k0 + u, kNB - 1) = hs;
+      hs = fmaf(P[u], hs, e[u]);
+    }
   }
   float rho = p.dh_final ? p.dh_final[bd * p.N + n] : 0.0f;
-  float l_next = sp[static_cast<int64_t>(p.nck - 1) * (kSlots * kNP) + kNB * kNP];
-  tot_next = cp[static_cast<int64_t>(p.nck - 1) * kNB];
-  for (int k = p.nck - 1; k >= 0; --k) {
-    float* const s = sp + static_cast<int64_t>(k) * (kSlots * kNP) + kNB * kNP;
-    const float lam = l_next, tot = tot_next;
-    if (k > 0) {
-      l_next = s[-kSlots * kNP];
-      tot_next = cp[static_cast<int64_t>(k - 1) * kNB];
+  for (int k1 = p.nck - 1; k1 >= 0; k1 -= U) {
+    float l[U], P[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = k1 - u >= 0;
+      l[u] = ok ? *slot(k1 - u, kNB) : 0.0f;
+      P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k1 - u) * kNB] * Ap) : 1.0f;
     }
-    *s = rho;
-    rho = fmaf(hw_exp2(tot * Ap), rho, lam);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k1 - u >= 0) *slot(k1 - u, kNB) = rho;
+      rho = fmaf(P[u], rho, l[u]);
+    }
   }
   if (p.dh0) p.dh0[bd * p.N + n] = rho;
 }
