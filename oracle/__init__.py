@@ -53,6 +53,8 @@ def _bind(path: str):
     lib.oracle_max_threads.restype = I
     lib.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64, I, I] + [P] * 20 + [I]
     lib.oracle_scan_bwd_f64.restype = I
+    lib.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 6 + [I]
+    lib.oracle_conv1d_f64.restype = I
     return lib
 
 
@@ -164,6 +166,24 @@ def scan_bwd(x, dt, A, B, C, dy, dt_bias=None, Dskip=None, z=None, h0=None, dh_f
     return out
 
 
+def conv1d(x, w, bias=None, state_in=None, silu=True, nthreads=0, _lib_override=None):
+    """Causal depthwise convolution of width K = w.shape[1] then SiLU: x (b, D, L), w (D, K), bias (D,), state_in
+    (b, D, K-1) = the inputs before t = 0, oldest first.  Returns (u (b, D, L), state_out (b, D, K-1))."""
+    x = _f64(x)
+    bsz, dim, L = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    bias = _f64(bias, (dim,))
+    state_in = _f64(state_in, (bsz, dim, K - 1))
+    u = np.zeros((bsz, dim, L))
+    st = np.zeros((bsz, dim, K - 1))
+    rc = (_lib_override or _load()).oracle_conv1d_f64(bsz, dim, L, K, int(bool(silu)), _ptr(x), _ptr(w), _ptr(bias),
+                                                      _ptr(state_in), _ptr(u), _ptr(st), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_conv1d_f64 failed with code %d" % rc)
+    return u, st
+
+
 class Oracle:
     """The oracle bound to a specific compiled library (the default one, or a test-built variant)."""
 
@@ -178,6 +198,9 @@ class Oracle:
 
     def scan_bwd(self, *a, **k):
         return scan_bwd(*a, _lib_override=self._lib, **k)
+
+    def conv1d(self, *a, **k):
+        return conv1d(*a, _lib_override=self._lib, **k)
 
 
 def compile_variant(src_text: str, out_path: str) -> str:

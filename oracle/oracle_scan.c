@@ -282,3 +282,52 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/*
+ * Causal depthwise convolution of width K over the sequence, then SiLU (test infrastructure, fp64).
+ * The Mamba block runs it on the SSM branch before the scan (docs.ifdog.com tutorial, "Mamba 架构", step 3a: a
+ * depthwise causal 1-D convolution of kernel size d_conv, usually 4, each channel on its own; the SiLU / Swish
+ * activation of the block, Mamba paper section 3.4).  Per batch b, channel d, step t:
+ *   xc_t = bias[d] + sum_{k=0}^{K-1} w[d][k] * x_{t-(K-1)+k},  x_tau for tau < 0 taken from state_in (oldest first;
+ *          zeros when state_in is NULL)
+ *   u_t  = silu(xc_t) = xc_t / (1 + exp(-xc_t))   (or xc_t when use_silu == 0)
+ *   state_out = the last K-1 inputs x_{L-K+1} .. x_{L-1} (oldest first), continuing from state_in when L < K-1.
+ * Layouts: x, u [batch][dim][seqlen]; w [dim][K]; bias [dim]; state_in, state_out [batch][dim][K-1].
+ */
+int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int use_silu, const double* x,
+                      const double* w, const double* bias, const double* state_in, double* u, double* state_out,
+                      int nthreads) {
+  if (batch < 0 || dim < 0 || seqlen < 1 || width < 1 || width > 64) return 1;
+  if (!x || !w || !u) return 2;
+  const int64_t K = width, S = width - 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t bd = 0; bd < batch * dim; ++bd) {
+    const int64_t d = bd % dim;
+    const double* xr = x + bd * seqlen;
+    const double* st = state_in ? state_in + bd * S : NULL;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t tau = t - (K - 1) + k;
+        const double xv = tau >= 0 ? xr[tau] : (st ? st[S + tau] : 0.0);
+        acc += w[d * K + k] * xv;
+      }
+      u[bd * seqlen + t] = use_silu ? acc / (1.0 + exp(-acc)) : acc;
+    }
+    if (state_out) {
+      double tmp[64];
+      for (int64_t i = 0; i < S; ++i) {
+        const int64_t tau = seqlen - S + i;
+        tmp[i] = tau >= 0 ? xr[tau] : (st ? st[S + tau] : 0.0);
+      }
+      for (int64_t i = 0; i < S; ++i) state_out[bd * S + i] = tmp[i];
+    }
+  }
+  return 0;
+}
+

@@ -326,6 +326,48 @@ def pin_bwd_finite_differences(orc, disc, seed=10):
         assert err < 2e-6, ("P10", disc, gk, err)
 
 
+# P11: causal depthwise conv1d (then SiLU).  The convolution against numpy.convolve (an independent implementation)
+#      over the zero- or state-padded sequence, every width 1..4; SiLU against closed forms.
+def pin_conv_numpy(orc, seed=11):
+    r = _rng(seed)
+    for K in (1, 2, 3, 4):
+        b, D, L = 2, 3, 37
+        x = r.standard_normal((b, D, L))
+        w = r.standard_normal((D, K))
+        bias = r.standard_normal(D)
+        st = r.standard_normal((b, D, K - 1)) if K > 1 else None
+        u, so = orc.conv1d(x, w, bias=bias, state_in=st, silu=False)
+        for bi in range(b):
+            for d in range(D):
+                pad = st[bi, d] if st is not None else np.zeros(0)
+                ref = np.convolve(np.concatenate([pad, x[bi, d]]), w[d][::-1], "valid") + bias[d]
+                assert np.max(np.abs(ref - u[bi, d])) < 1e-12, ("P11", K)
+                if K > 1:
+                    assert np.array_equal(so[bi, d], x[bi, d, L - (K - 1):]), ("P11 state", K)
+    # SiLU: w = 0, bias = ln 3 -> sigmoid = 3/4, u = 0.75 ln 3; bias = -ln 3 -> u = -0.25 ln 3; bias = 0 -> 0
+    w = np.zeros((3, 4))
+    for bv, want in ((np.log(3.0), 0.75 * np.log(3.0)), (-np.log(3.0), -0.25 * np.log(3.0)), (0.0, 0.0)):
+        u, _ = orc.conv1d(np.ones((1, 3, 5)), w, bias=np.full(3, bv), silu=True)
+        assert np.max(np.abs(u - want)) < 1e-15, ("P11 silu", bv)
+
+
+# P12: streaming: the convolution of a sequence equals the convolution of its two halves, the second continuing from
+#      the first's state; a sequence shorter than the state shifts the state (closed form).
+def pin_conv_split(orc, seed=12):
+    r = _rng(seed)
+    x = r.standard_normal((2, 4, 50))
+    w = r.standard_normal((4, 4))
+    bias = r.standard_normal(4)
+    st = r.standard_normal((2, 4, 3))
+    u, so = orc.conv1d(x, w, bias=bias, state_in=st)
+    u1, s1 = orc.conv1d(x[:, :, :21], w, bias=bias, state_in=st)
+    u2, s2 = orc.conv1d(x[:, :, 21:], w, bias=bias, state_in=s1)
+    assert np.max(np.abs(np.concatenate([u1, u2], axis=2) - u)) < 1e-14, "P12"
+    assert np.array_equal(s2, so), "P12 state"
+    u3, s3 = orc.conv1d(x[:, :, :1], w, bias=bias, state_in=st)
+    assert np.array_equal(s3, np.concatenate([st[:, :, 1:], x[:, :, :1]], axis=2)), "P12 short"
+
+
 def all_pins(orc, worked_rows):
     """Run every pin; returns a list of (name, error-or-None)."""
     out = []
@@ -341,6 +383,7 @@ def all_pins(orc, worked_rows):
                    ("reset_hold_%d" % disc, lambda disc=disc: pin_reset_hold(orc, disc)),
                    ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
                    ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
+    out += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc))]
     for name, fn in checks:
         try:
             fn()

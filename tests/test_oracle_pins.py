@@ -77,6 +77,14 @@ def test_backward_without_optional_parts(orc):
     assert abs(fd - g["dx"][0, 1, 3]) < 1e-7
 
 
+def test_conv_numpy(orc):
+    pins.pin_conv_numpy(orc)
+
+
+def test_conv_split(orc):
+    pins.pin_conv_split(orc)
+
+
 def test_softplus_tails(orc):
     # Delta for very negative / positive logits: log1p(e^u) ~ e^u and ~ u + e^-u (no cancellation, no overflow).
     u = np.array([-40.0, -12.0, 0.0, 12.0, 40.0, 700.0])
@@ -118,6 +126,12 @@ MUTANTS = [
     ("bwd_softplus_derivative", r"dDelta \* sigm\(u\)", "dDelta * sigm(-u)"),
     ("bwd_silu_derivative", r"\(sg \* \(1\.0 \+ zv \* \(1\.0 - sg\)\)\)", "sg"),
     ("bwd_zoh_dA_series", r"0\.5 \+ e \* \(1\.0 / 3\.0", "0.5 + e * (1.0 / 2.0"),
+    ("conv_taps_reversed", r"acc \+= w\[d \* K \+ k\] \* xv;", "acc += w[d * K + (K - 1 - k)] * xv;"),
+    ("conv_state_ignored", r"const double xv = tau >= 0 \? xr\[tau\] : \(st \? st\[S \+ tau\] : 0\.0\);",
+     "const double xv = tau >= 0 ? xr[tau] : 0.0;"),
+    ("conv_bias_dropped", r"double acc = bias \? bias\[d\] : 0\.0;", "double acc = 0.0;"),
+    ("conv_state_out_shift", r"const int64_t tau = seqlen - S \+ i;", "const int64_t tau = seqlen - S + i - 1;"),
+    ("conv_sigmoid_not_silu", r"use_silu \? acc / \(1\.0 \+ exp\(-acc\)\)", "use_silu ? 1.0 / (1.0 + exp(-acc))"),
 ]
 
 
