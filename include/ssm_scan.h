@@ -76,7 +76,26 @@ typedef struct {
   int32_t reserved;    /* must be 0 */
 } ssm_scan_params;
 
-/* Bytes of device workspace ssm_scan_fwd needs for these parameters (0 when none).  Pure host function. */
+/*
+ * Causal depthwise convolution in front of the scan (the Mamba block's SSM branch: docs.ifdog.com tutorial, "Mamba 架构"
+ * step 3a -- a 1-D causal convolution of kernel size d_conv, usually 4, each channel on its own -- followed by the
+ * block's SiLU activation, Mamba paper section 3.4).  With it the scan's input x is replaced by
+ *   u[b,d,t] = act(bias[d] + sum_{k=0}^{width-1} weight[d][k] * x[b,d,t-(width-1)+k]),   act = SiLU or identity,
+ * where x before t = 0 comes from state_in (oldest first; zeros when NULL).  u feeds both the recurrence and the D
+ * skip; it is computed in the scan kernel and never written to memory.
+ */
+typedef struct {
+  const float* weight;   /* [dim][width] fp32, required */
+  const float* bias;     /* [dim] fp32 or NULL (= 0) */
+  const float* state_in; /* [batch][dim][width-1] fp32 or NULL (= zeros): the inputs before the first step */
+  float* state_out;      /* [batch][dim][width-1] fp32 or NULL: the last width-1 inputs (continuing state_in when
+                            seqlen < width-1), oldest first; may alias state_in */
+  int32_t width;         /* 1 <= width <= 4 */
+  int32_t activation;    /* 1: SiLU after the convolution; 0: none */
+} ssm_conv_params;
+
+/* Bytes of device workspace ssm_scan_fwd needs for these parameters (0 when none).  Pure host function.
+ * ssm_conv_scan_fwd needs the same workspace. */
 size_t ssm_scan_fwd_workspace_bytes(const ssm_scan_params* p);
 
 /*
@@ -101,6 +120,25 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt,
 ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* x, const void* dt,
                             const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
                             const void* z, void* y, void* stream);
+
+/*
+ * ssm_scan_fwd with the causal convolution (+ activation) above applied to x first.  x [batch][dim][seqlen] io_dtype
+ * is the convolution's input; every other argument is as for ssm_scan_fwd.  conv->state_out, if given, is written
+ * after the scan has read conv->state_in, so the two may alias.
+ */
+ssm_status ssm_conv_scan_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, const void* x, const void* dt,
+                             const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
+                             const void* z, const float* h0, void* y, float* h_final, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_state_update with the causal convolution: the convolution window of the last width-1 inputs is read from
+ * conv->state_in and the shifted window (ending with this step's x) written to conv->state_out (both required for
+ * width > 1; they may alias, which updates the window in place).  One step of ssm_conv_scan_fwd.
+ */
+ssm_status ssm_conv_state_update(const ssm_scan_params* p, const ssm_conv_params* conv, float* state, const void* x,
+                                 const void* dt, const float* dt_bias, const float* A, const void* B, const void* C,
+                                 const float* Dskip, const void* z, void* y, void* stream);
 
 /* Bytes of device workspace ssm_scan_bwd needs for these parameters (always > 0 for valid parameters, 0 for invalid
  * ones).  Pure host function. */

@@ -1,7 +1,9 @@
 """MI355X-native S6 selective scan (Mamba's selective SSM: forward pass, backward pass and single-token decode).
 
 ``scan_fwd``, ``scan_bwd`` and ``state_update`` call the C ABI of libssm57.so (include/ssm_scan.h) on PyTorch device
-tensors; the arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded synthetic workloads.
+tensors; ``conv_scan_fwd`` and ``conv_state_update`` do the same with the block's causal depthwise convolution + SiLU
+applied to x inside the kernels.  The arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded
+synthetic workloads.
 """
 from __future__ import annotations
 
@@ -9,8 +11,8 @@ from . import _abi
 from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_params, workspace_bytes, plan_segments,
                    bwd_workspace_bytes)
 
-__all__ = ["scan_fwd", "scan_bwd", "state_update", "EULER_B", "ZOH", "SSMError", "Params", "make_params",
-           "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "EULER_B", "ZOH", "SSMError",
+           "Params", "make_params", "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
 def io_code(dtype) -> int:
@@ -149,6 +151,84 @@ def scan_bwd(x, dt, A, B, C, dy, dt_bias=None, Dskip=None, z=None, h0=None, dh_f
                            _stream_handle(stream, dev))
     _abi.check(st)
     return o
+
+
+def _conv_params(conv_w, conv_bias, conv_state, conv_state_out, activation, D, b, dev):
+    import torch
+    f32 = torch.float32
+    if conv_w is None or conv_w.dim() != 2 or conv_w.shape[0] != D:
+        raise ValueError("conv_w: expected shape (%d, width)" % D)
+    K = conv_w.shape[1]
+    _expect("conv_w", conv_w, (D, K), f32, dev, optional=False)
+    _expect("conv_bias", conv_bias, (D,), f32, dev)
+    _expect("conv_state", conv_state, (b, D, K - 1), f32, dev)
+    _expect("conv_state_out", conv_state_out, (b, D, K - 1), f32, dev)
+    return _abi.make_conv(_addr(conv_w), K, _addr(conv_bias), _addr(conv_state), _addr(conv_state_out),
+                          int(bool(activation)))
+
+
+def conv_scan_fwd(x, conv_w, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, conv_bias=None,
+                  conv_state=None, conv_state_out=None, activation=True, y=None, h_final=None, y_dtype=None,
+                  disc=EULER_B, softplus=True, segments=0, workspace=None, return_final_state=True, stream=None):
+    """The scan of u = silu(causal_conv(x)) (activation=False: no SiLU): conv_w (D, width <= 4) float32, conv_bias
+    (D,), conv_state (b, D, width-1) the inputs before step 0 (oldest first).  ``conv_state_out`` (may be conv_state)
+    receives the last width-1 inputs.  Everything else as for ``scan_fwd``.  Returns (y, h_final)."""
+    import torch
+    b, D, L = x.shape
+    N = A.shape[1]
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("x", x, (b, D, L), x.dtype, False), ("dt", dt, (b, D, L), x.dtype, False),
+                                   ("z", z, (b, D, L), x.dtype, True), ("B", B, (b, N, L), x.dtype, False),
+                                   ("C", C, (b, N, L), x.dtype, False), ("A", A, (D, N), f32, False),
+                                   ("dt_bias", dt_bias, (D,), f32, True), ("Dskip", Dskip, (D,), f32, True),
+                                   ("h0", h0, (b, D, N), f32, True), ("y", y, (b, D, L), ydt, True),
+                                   ("h_final", h_final, (b, D, N), f32, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    cp = _conv_params(conv_w, conv_bias, conv_state, conv_state_out, activation, D, b, dev)
+    p = make_params(b, D, L, N, io, io_code(ydt), disc, softplus, segments)
+    if y is None:
+        y = torch.empty((b, D, L), dtype=ydt, device=dev)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((b, D, N), dtype=f32, device=dev)
+    need = workspace_bytes(p)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _abi.conv_scan_fwd_raw(p, cp, _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C),
+                                _addr(Dskip), _addr(z), _addr(h0), _addr(y), _addr(h_final), _addr(workspace),
+                                ws_bytes, _stream_handle(stream, dev))
+    _abi.check(st)
+    return y, h_final
+
+
+def conv_state_update(state, conv_state, x, conv_w, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *,
+                      conv_bias=None, activation=True, y=None, y_dtype=None, disc=EULER_B, softplus=True,
+                      stream=None):
+    """One decode step through the convolution: state (b, D, N) and conv_state (b, D, width-1) float32 are both updated
+    in place; x, dt, z: (b, D); B, C: (b, N).  Returns y (b, D)."""
+    import torch
+    b, D, N = state.shape
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("state", state, (b, D, N), f32, False), ("x", x, (b, D), x.dtype, False),
+                                   ("dt", dt, (b, D), x.dtype, False), ("z", z, (b, D), x.dtype, True),
+                                   ("B", B, (b, N), x.dtype, False), ("C", C, (b, N), x.dtype, False),
+                                   ("A", A, (D, N), f32, False), ("dt_bias", dt_bias, (D,), f32, True),
+                                   ("Dskip", Dskip, (D,), f32, True), ("y", y, (b, D), ydt, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    cp = _conv_params(conv_w, conv_bias, conv_state, conv_state, activation, D, b, dev)
+    p = make_params(b, D, 1, N, io, io_code(ydt), disc, softplus, 0)
+    if y is None:
+        y = torch.empty((b, D), dtype=ydt, device=dev)
+    st = _abi.conv_state_update_raw(p, cp, _addr(state), _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B),
+                                    _addr(C), _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, dev))
+    _abi.check(st)
+    return y
 
 
 def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=None, y_dtype=None, disc=EULER_B,

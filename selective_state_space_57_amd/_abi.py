@@ -16,7 +16,8 @@ EULER_B, ZOH = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_UNSUPPORTED",
           5: "SSM_ERR_ALIGN", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_HIP"}
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
-           "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd"]
+           "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
+           "ssm_conv_scan_fwd", "ssm_conv_state_update"]
 
 
 class Params(ctypes.Structure):
@@ -24,6 +25,11 @@ class Params(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
                 ("disc", ctypes.c_int32), ("dt_softplus", ctypes.c_int32), ("segments", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class ConvParams(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("state_in", ctypes.c_void_p),
+                ("state_out", ctypes.c_void_p), ("width", ctypes.c_int32), ("activation", ctypes.c_int32)]
 
 
 class SSMError(RuntimeError):
@@ -58,6 +64,11 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.restype = S
         L.ssm_scan_bwd.argtypes = [PP] + [P] * 20 + [P, S, P]
         L.ssm_scan_bwd.restype = ctypes.c_int
+        CP = ctypes.POINTER(ConvParams)
+        L.ssm_conv_scan_fwd.argtypes = [PP, CP] + [P] * 11 + [P, S, P]
+        L.ssm_conv_scan_fwd.restype = ctypes.c_int
+        L.ssm_conv_state_update.argtypes = [PP, CP] + [P] * 11
+        L.ssm_conv_state_update.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -90,6 +101,22 @@ def scan_fwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, w
     """Direct call with integer device addresses (0 = NULL)."""
     return lib().ssm_scan_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
                               workspace_bytes_, stream)
+
+
+def make_conv(weight, width, bias=0, state_in=0, state_out=0, activation=1) -> ConvParams:
+    """Conv parameters from integer device addresses (0 = NULL)."""
+    return ConvParams(weight, bias, state_in, state_out, int(width), int(activation))
+
+
+def conv_scan_fwd_raw(p: Params, conv: ConvParams, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
+                      workspace_bytes_, stream):
+    return lib().ssm_conv_scan_fwd(ctypes.byref(p), ctypes.byref(conv), x, dt, dt_bias, A, B, C, Dskip, z, h0, y,
+                                   h_final, workspace, workspace_bytes_, stream)
+
+
+def conv_state_update_raw(p: Params, conv: ConvParams, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):
+    return lib().ssm_conv_state_update(ctypes.byref(p), ctypes.byref(conv), state, x, dt, dt_bias, A, B, C, Dskip, z,
+                                       y, stream)
 
 
 def bwd_workspace_bytes(p: Params) -> int:

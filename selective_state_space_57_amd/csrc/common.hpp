@@ -131,6 +131,13 @@ __device__ __forceinline__ float row_bcast(float v) {
                                                                false));
 }
 
+// value of lane (i - K) mod 16 of each 16-lane row (DPP row_ror)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + K, 0xf, 0xf,
+                                                               false));
+}
+
 template <typename F, int... Ks>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
   (f(std::integral_constant<int, Ks>{}), ...);

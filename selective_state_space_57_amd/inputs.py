@@ -13,7 +13,9 @@ Recipe (also written out in the design doc):
   * every tensor k of workload `cfg` at decode step `step` is drawn in flattened chunks of 2**24 elements, chunk i
     from numpy's default_rng(SeedSequence(57, spawn_key=(cfg, step, k, i)));
   * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state, 9 dy, 10 dh_final
-    (the last two are the cotangents fed to the backward pass);
+    (the cotangents fed to the backward pass), 11 conv weight, 12 conv bias, 13 conv state (the causal convolution
+    in front of the scan: weight and bias U(-1/sqrt(width), 1/sqrt(width)), the default init of a 1-D convolution
+    with one input channel per group; state N(0, 1));
   * normals are numpy float32 standard normals; log-uniforms are exp(uniform(log lo, log hi)) in float64;
   * Delta-logit = softplus^-1(Delta*) - bias[d], with softplus^-1(v) = log(expm1(v)), rounded to the io dtype;
   * bf16 values are rounded to nearest-even from float32 (float64 -> float32 -> bf16 for float64 sources).
@@ -235,6 +237,22 @@ def random_small_cotangents(seed: int, b: int, D: int, L: int, N: int, io: str =
     """Cotangents matching random_small(seed, ...)."""
     w = Workload("small", b, D, L, N, io, 1e-3, 1e-1, 0.0, cfg_id=1000 + seed)
     return cotangents(w, io=io, with_dh_final=dh_final)
+
+
+def conv_params(w: Workload, width: int = 4, with_state: bool = False) -> dict:
+    """Causal convolution parameters for workload w: weight (D, width), bias (D,), state (b, D, width-1) or None."""
+    c, D = w.cfg_id, w.dim
+    bound = 1.0 / np.sqrt(width)
+    wt = (_rng(c, 0, 11, 0).uniform(-bound, bound, D * width)).astype(np.float32).reshape(D, width)
+    bias = _rng(c, 0, 12, 0).uniform(-bound, bound, D).astype(np.float32)
+    st = _normal(c, 0, 13, w.batch * D * (width - 1)).reshape(w.batch, D, width - 1) if with_state else None
+    return {"conv_w": wt, "conv_b": bias, "conv_state": st}
+
+
+def random_small_conv(seed: int, b: int, D: int, N: int, width: int = 4, with_state: bool = False) -> dict:
+    """Convolution parameters matching random_small(seed, ...)."""
+    w = Workload("small", b, D, 1, N, F32, 1e-3, 1e-1, 0.0, cfg_id=1000 + seed)
+    return conv_params(w, width, with_state)
 
 
 def decode_state(w: Workload) -> np.ndarray:

@@ -131,3 +131,29 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _abi.lib()
+
+
+def call_conv_scan(p, conv, **ptrs):
+    names = ["x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "h0", "y", "h_final"]
+    v = {k: FAKE for k in ["x", "dt", "A", "B", "C", "y"]}
+    v.update(ptrs)
+    return _abi.conv_scan_fwd_raw(p, conv, *[v.get(k, 0) for k in names], 0, 0, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(weight=0), 1), (dict(width=0), 4), (dict(width=5), 4), (dict(activation=2), 4), (dict(weight=FAKE + 2), 5),
+])
+def test_conv_param_errors(lib, kw, code):
+    base = dict(weight=FAKE, width=4, bias=0, state_in=0, state_out=0, activation=1)
+    base.update(kw)
+    conv = _abi.make_conv(**base)
+    assert call_conv_scan(P(), conv) == code
+    assert lib.ssm_last_error().decode()
+
+
+def test_conv_decode_needs_window(lib):
+    conv = _abi.make_conv(FAKE, 4)
+    names = ["state", "x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "y"]
+    v = {k: FAKE for k in ["state", "x", "dt", "A", "B", "C", "y"]}
+    assert _abi.conv_state_update_raw(P(), conv, *[v.get(k, 0) for k in names], 0) == 1
+

@@ -1,0 +1,134 @@
+"""GPU parity of the scan fed through the causal depthwise convolution + SiLU (ssm_conv_scan_fwd) and of its decode
+step (ssm_conv_state_update), against the fp64 oracle: oracle.conv1d followed by oracle.scan on its output."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_57_amd as ssm
+from selective_state_space_57_amd import inputs as I
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def ref_conv_scan(d, cv, disc=0, silu=True, softplus=True):
+    f = I.as_f64(d)
+    st = None if cv["conv_state"] is None else cv["conv_state"].astype(np.float64)
+    u, so = oracle.conv1d(f["x"], cv["conv_w"].astype(np.float64), bias=cv["conv_b"].astype(np.float64),
+                          state_in=st, silu=silu)
+    y, h = oracle.scan(u, f["dt"], f["A"], f["B"], f["C"], dt_bias=f["dt_bias"], Dskip=f["Dskip"], z=f["z"],
+                       h0=f["h0"], disc=disc, softplus=softplus)
+    return y, h, so
+
+
+def run_conv_scan(dd, dc, disc=0, silu=True, segments=0, state_out=None):
+    torch = G.torch_dev()
+    y, hf = ssm.conv_scan_fwd(dd["x"], dc["conv_w"], dd["dt"], dd["A"], dd["B"], dd["C"], dt_bias=dd["dt_bias"],
+                              Dskip=dd["Dskip"], z=dd["z"], h0=dd["h0"], conv_bias=dc["conv_b"],
+                              conv_state=dc["conv_state"], conv_state_out=state_out, activation=silu,
+                              y_dtype=torch.float32, disc=disc, segments=segments)
+    torch.cuda.synchronize()
+    return y, hf
+
+
+@pytest.mark.parametrize("seed,b,D,L,N,io,width,state,silu,disc,segments", [
+    (1, 1, 16, 64, 16, "f32", 4, False, True, 0, 0),
+    (2, 2, 17, 100, 16, "f32", 4, True, True, 0, 0),
+    (3, 2, 33, 257, 16, "bf16", 4, True, True, 0, 0),
+    (4, 1, 5, 1, 16, "f32", 4, True, True, 0, 0),      # one step: the whole window comes from the state
+    (5, 2, 9, 2, 16, "f32", 3, True, True, 1, 0),      # shorter than the window, ZOH
+    (6, 1, 20, 130, 5, "f32", 2, True, False, 0, 0),   # width 2, no activation, N = 5
+    (7, 3, 12, 77, 16, "bf16", 1, False, True, 0, 0),  # width 1: a per-channel scale + bias + SiLU
+    (8, 2, 19, 700, 16, "f32", 4, True, True, 0, 4),   # four L-segments: windows across segment starts
+    (9, 1, 64, 1500, 16, "bf16", 4, False, True, 1, 3),
+])
+def test_conv_scan_random(seed, b, D, L, N, io, width, state, silu, disc, segments):
+    torch = G.torch_dev()
+    d = I.random_small(seed, b, D, L, N, io=io, h0=True)
+    cv = I.random_small_conv(seed, b, D, N, width=width, with_state=state)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    so = torch.empty((b, D, width - 1), dtype=torch.float32, device="cuda") if width > 1 else None
+    y, hf = run_conv_scan(dd, dc, disc=disc, silu=silu, segments=segments, state_out=so)
+    yr, hr, sr = ref_conv_scan(d, cv, disc=disc, silu=silu)
+    tol = G.tol_for(io)
+    assert G.rel_max(G.to_np64(y), yr) <= tol
+    assert G.rel_max(G.to_np64(hf), hr) <= tol
+    if so is not None:
+        assert np.array_equal(so.cpu().numpy().astype(np.float64), sr)  # the window is copied, not computed
+
+
+def test_conv_state_out_may_alias_state_in():
+    torch = G.torch_dev()
+    d = I.random_small(20, 2, 11, 50, 16, io="f32", h0=True)
+    cv = I.random_small_conv(20, 2, 11, 16, width=4, with_state=True)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    yr, hr, sr = ref_conv_scan(d, cv)
+    y, _ = run_conv_scan(dd, dc, state_out=dc["conv_state"])  # in place
+    assert G.rel_max(G.to_np64(y), yr) <= G.TOL_F32
+    assert np.array_equal(dc["conv_state"].cpu().numpy().astype(np.float64), sr)
+
+
+def test_conv_split_sequence_hand_off():
+    # two calls with the windows and states handed over equal one call over the whole sequence
+    torch = G.torch_dev()
+    d = I.random_small(21, 2, 24, 300, 16, io="f32", h0=True)
+    cv = I.random_small_conv(21, 2, 24, 16, width=4, with_state=True)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    y_full, h_full = run_conv_scan(dd, dc)
+    first = {k: (v[:, :, :128].contiguous() if k in ("x", "dt", "z", "B", "C") else v) for k, v in dd.items()}
+    second = {k: (v[:, :, 128:].contiguous() if k in ("x", "dt", "z", "B", "C") else v) for k, v in dd.items()}
+    mid = torch.empty_like(dc["conv_state"])
+    y1, h1 = run_conv_scan(first, dc, state_out=mid)
+    second["h0"] = h1
+    y2, h2 = run_conv_scan(second, dict(dc, conv_state=mid))
+    yy = torch.cat([y1, y2], dim=2)
+    assert G.rel_max(G.to_np64(yy), G.to_np64(y_full)) <= 1e-6
+    assert G.rel_max(G.to_np64(h2), G.to_np64(h_full)) <= 1e-6
+
+
+@pytest.mark.parametrize("io,width,disc", [("f32", 4, 0), ("bf16", 4, 1), ("f32", 2, 0)])
+def test_conv_decode_equals_conv_scan(io, width, disc):
+    torch = G.torch_dev()
+    T = 40
+    d = I.random_small(30 + width, 3, 45, T, 16, io=io, h0=True)
+    cv = I.random_small_conv(30 + width, 3, 45, 16, width=width, with_state=True)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    y_scan, h_scan = run_conv_scan(dd, dc, disc=disc)
+    state = dd["h0"].clone()
+    win = dc["conv_state"].clone()
+    ys = []
+    for t in range(T):
+        sl = lambda k: dd[k][:, :, t].contiguous()
+        ys.append(ssm.conv_state_update(state, win, sl("x"), dc["conv_w"], sl("dt"), dd["A"], sl("B"), sl("C"),
+                                        dt_bias=dd["dt_bias"], Dskip=dd["Dskip"], z=sl("z"), conv_bias=dc["conv_b"],
+                                        y_dtype=torch.float32, disc=disc))
+    torch.cuda.synchronize()
+    yd = torch.stack(ys, dim=2)
+    assert G.rel_max(G.to_np64(yd), G.to_np64(y_scan)) <= 1e-5
+    assert G.rel_max(G.to_np64(state), G.to_np64(h_scan)) <= 1e-5
+    yr, hr, sr = ref_conv_scan(d, cv, disc=disc)
+    assert G.rel_max(G.to_np64(yd), yr) <= G.tol_for(io)
+    assert np.array_equal(win.cpu().numpy().astype(np.float64), sr)
+
+
+def test_conv_scan_full_size_sampled():
+    """The 2.8B layer with the width-4 convolution, in the benchmark's launch configuration, checked on sampled
+    channels (each channel's output depends only on its own inputs)."""
+    torch = G.torch_dev()
+    w = I.WORKLOADS[2]
+    d = I.scan_inputs(w)
+    cv = I.conv_params(w, 4)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    y, hf = run_conv_scan(dd, dc)
+    chans = G.sample_channels(w.batch, w.dim, 24, seed=5)
+    got = np.stack([G.to_np64(y[b, dd_]) for b, dd_ in chans])
+    ref = []
+    for (bi, di) in chans:
+        sub = {k: (None if v is None else
+                   (v[bi:bi + 1, di:di + 1] if k in ("x", "dt", "z", "h0") else
+                    (v[di:di + 1] if k in ("A", "dt_bias", "Dskip") else v[bi:bi + 1])))
+               for k, v in d.items()}
+        scv = {"conv_w": cv["conv_w"][di:di + 1], "conv_b": cv["conv_b"][di:di + 1], "conv_state": None}
+        yr, _, _ = ref_conv_scan(sub, scv)
+        ref.append(yr[0, 0])
+    assert G.rel_max(got, np.stack(ref)) <= G.TOL_BF16
