@@ -44,6 +44,11 @@ def scan_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
     return 2.0 * per_elem * b * D * L
 
 
+def conv_algorithmic_flops(b, D, L, width=4):
+    """The causal convolution + SiLU in front of the scan, per (b, d, t): width FMAs, SiLU = exp + rcp (4 slots) + 2."""
+    return 2.0 * (width + 6) * b * D * L
+
+
 def bwd_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
     """fp32 work of the backward per (b, d, t), in FMA-slot units x 2 FLOP (same convention as the forward).
     Per state n: zero-start chunk pass 8 (Delta*A, exp 2, (Delta x)*B, h FMA, decay product, C*ds, lambda FMA);
@@ -114,6 +119,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (torch) five times: the reference kernel "
@@ -207,6 +213,40 @@ def main():
                      "kernel": kernel_key, "algorithmic_flops": flops},
         "host_wall_ms_timed_region": wall_ms,
     }
+
+    # ---- the same forward with the block's causal convolution (width 4) + SiLU fused in front of the scan
+    if not args.no_conv:
+        from selective_state_space_57_amd import _abi
+        cvp = I.conv_params(w, 4)
+        cw, cb = up(cvp["conv_w"]), up(cvp["conv_b"])
+        conv = _abi.make_conv(cw.data_ptr(), 4, cb.data_ptr(), 0, 0, 1)
+        cargs = (d["x"].data_ptr(), d["dt"].data_ptr(), d["dt_bias"].data_ptr(), d["A"].data_ptr(),
+                 d["B"].data_ptr(), d["C"].data_ptr(), d["Dskip"].data_ptr(), d["z"].data_ptr(), 0, y.data_ptr(),
+                 hf.data_ptr(), ws.data_ptr() if ws_n else 0, ws_n, stream.cuda_stream)
+
+        def cstep():
+            st = _abi.conv_scan_fwd_raw(p, conv, *cargs)
+            if st:
+                _abi.check(st)
+
+        for _ in range(5):
+            cstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            cstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / args.steps
+        cfl = flops + conv_algorithmic_flops(b, D, L, 4)
+        out["conv_scan"] = {"workload": "mamba2.8b-layer + causal conv1d (width 4) + SiLU", "ms_per_step": cms,
+                            "elements_per_s": elems / (cms * 1e-3), "overhead_vs_scan": cms / ms - 1.0,
+                            "algorithmic_flops": cfl, "achieved_TFLOPs": cfl / (cms * 1e-3) / 1e12,
+                            "frac_of_valu_peak": cfl / (cms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS,
+                            "algorithmic_bytes": nbytes + D * 4 * 5,
+                            "note": "x is read once and the convolved sequence never goes to memory; a separate "
+                                    "convolution kernel would add a write and a read of it (2 x 168 MB in bf16)"}
 
     # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
     if not args.no_bwd:
