@@ -55,6 +55,10 @@ def _bind(path: str):
     lib.oracle_scan_bwd_f64.restype = I
     lib.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 6 + [I]
     lib.oracle_conv1d_f64.restype = I
+    lib.oracle_complex_scan_f64.argtypes = [I64, I64, I64, I64, I, I] + [P] * 11 + [I]
+    lib.oracle_complex_scan_f64.restype = I
+    lib.oracle_complex_state_update_f64.argtypes = [I64, I64, I64, I, I] + [P] * 10
+    lib.oracle_complex_state_update_f64.restype = I
     return lib
 
 
@@ -72,6 +76,19 @@ def _f64(a, shape=None):
     a = np.ascontiguousarray(a, dtype=np.float64)
     if shape is not None and a.shape != tuple(shape):
         raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _cplx(a, shape=None):
+    """complex (or real with a trailing axis of 2) -> contiguous float64 (..., 2); None stays None."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if np.iscomplexobj(a):
+        a = np.stack([a.real, a.imag], axis=-1)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape) + (2,):
+        raise ValueError("expected shape %s + (2,), got %s" % (tuple(shape), a.shape))
     return a
 
 
@@ -184,6 +201,47 @@ def conv1d(x, w, bias=None, state_in=None, silu=True, nthreads=0, _lib_override=
     return u, st
 
 
+def complex_scan(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, disc=EULER_B, softplus=True, nthreads=0,
+                 _lib_override=None):
+    """Complex diagonal A: A (D, N) complex, B, C (b, N, L) complex, h0 (b, D, N) complex (numpy complex arrays or
+    real arrays with a last axis of 2).  Returns (y (b, D, L) real, h_final (b, D, N) complex)."""
+    x = _f64(x)
+    bsz, dim, L = x.shape
+    A = _cplx(A)
+    N = A.shape[1]
+    dt = _f64(dt, (bsz, dim, L))
+    B = _cplx(B, (bsz, N, L))
+    C = _cplx(C, (bsz, N, L))
+    dt_bias = _f64(dt_bias, (dim,))
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, (bsz, dim, L))
+    h0 = _cplx(h0, (bsz, dim, N))
+    y = np.zeros((bsz, dim, L))
+    hf = np.zeros((bsz, dim, N, 2))
+    rc = (_lib_override or _load()).oracle_complex_scan_f64(
+        bsz, dim, L, N, int(disc), int(bool(softplus)), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_complex_scan_f64 failed with code %d" % rc)
+    return y, hf[..., 0] + 1j * hf[..., 1]
+
+
+def complex_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, disc=EULER_B, softplus=True,
+                         _lib_override=None):
+    """One complex decode step: state (b, D, N) complex -> (y (b, D), new state)."""
+    st = _cplx(state).copy()
+    bsz, dim, N = st.shape[:3]
+    x = _f64(x)
+    y = np.zeros((bsz, dim))
+    rc = (_lib_override or _load()).oracle_complex_state_update_f64(
+        bsz, dim, N, int(disc), int(bool(softplus)), _ptr(st), _ptr(x), _ptr(_f64(dt, (bsz, dim))),
+        _ptr(_f64(dt_bias, (dim,))), _ptr(_cplx(A)), _ptr(_cplx(B, (bsz, N))), _ptr(_cplx(C, (bsz, N))),
+        _ptr(_f64(Dskip, (dim,))), _ptr(_f64(z, (bsz, dim))), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_complex_state_update_f64 failed with code %d" % rc)
+    return y, st[..., 0] + 1j * st[..., 1]
+
+
 class Oracle:
     """The oracle bound to a specific compiled library (the default one, or a test-built variant)."""
 
@@ -201,6 +259,12 @@ class Oracle:
 
     def conv1d(self, *a, **k):
         return conv1d(*a, _lib_override=self._lib, **k)
+
+    def complex_scan(self, *a, **k):
+        return complex_scan(*a, _lib_override=self._lib, **k)
+
+    def complex_state_update(self, *a, **k):
+        return complex_state_update(*a, _lib_override=self._lib, **k)
 
 
 def compile_variant(src_text: str, out_path: str) -> str:

@@ -331,3 +331,99 @@ int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
   return 0;
 }
 
+/*
+ * Complex diagonal A (test infrastructure, fp64).  The Mamba paper (section 3.6, "real vs. complex") keeps a complex
+ * state for continuous modalities and initialises A with S4D-Lin, A_n = -1/2 + n i (audio experiments, section 4.4).
+ * Same recurrence as oracle_scan_f64 in complex arithmetic, with B and C complex and a real output:
+ *   Abar = exp(Delta A)  (complex exponential),  Bbar = Delta B (Euler-B) or (exp(Delta A) - 1) / A * B (ZOH; A = 0
+ *   gives Delta B),  h_t = Abar h_{t-1} + Bbar x_t,  y_t = Re(sum_n C_n h_n) + Dskip x_t, times silu(z_t).
+ * Complex arrays are interleaved (re, im) on a last axis of 2: A [dim][dstate][2]; B, C [batch][dstate][seqlen][2];
+ * h0, h_final, decode state [batch][dim][dstate][2].  x, dt, z, y, dt_bias, Dskip as in oracle_scan_f64.
+ */
+static void cstep(int64_t N, int disc, int use_softplus, double xv, double dtv, double bias, const double* A_row,
+                  const double* Bt, int64_t bstride, const double* Ct, double* h, double* yout) {
+  const double u = dtv + bias;
+  const double delta = use_softplus ? sp(u) : u;
+  double y = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    const double ar = A_row[2 * n], ai = A_row[2 * n + 1];
+    const double mag = exp(delta * ar), ang = delta * ai;
+    const double abr = mag * cos(ang), abi = mag * sin(ang);  /* Abar = exp(Delta A) */
+    const double br = Bt[n * bstride], bi = Bt[n * bstride + 1];
+    double cr, ci;                                           /* coefficient of B */
+    if (disc == 0 || (ar == 0.0 && ai == 0.0)) {
+      cr = delta;
+      ci = 0.0;
+    } else {                                                 /* (Abar - 1) / A, with expm1 for the real part */
+      const double er = expm1(delta * ar) * cos(ang) - 2.0 * sin(0.5 * ang) * sin(0.5 * ang);  /* Re(Abar) - 1 */
+      const double ei = abi;
+      const double den = ar * ar + ai * ai;
+      cr = (er * ar + ei * ai) / den;
+      ci = (ei * ar - er * ai) / den;
+    }
+    const double bbr = (cr * br - ci * bi) * xv, bbi = (cr * bi + ci * br) * xv;
+    const double hr = h[2 * n], hi = h[2 * n + 1];
+    h[2 * n] = abr * hr - abi * hi + bbr;
+    h[2 * n + 1] = abr * hi + abi * hr + bbi;
+    y += Ct[n * bstride] * h[2 * n] - Ct[n * bstride + 1] * h[2 * n + 1];
+  }
+  *yout = y;
+}
+
+int oracle_complex_scan_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int disc, int use_softplus,
+                            const double* x, const double* dt, const double* dt_bias, const double* A, const double* B,
+                            const double* C, const double* Dskip, const double* z, const double* h0, double* y,
+                            double* h_final, int nthreads) {
+  if (batch < 0 || dim < 0 || seqlen < 1 || dstate < 1 || dstate > 4096) return 1;
+  if (!x || !dt || !A || !B || !C || !y) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t N = dstate, L = seqlen;
+#pragma omp parallel for schedule(static)
+  for (int64_t bd = 0; bd < batch * dim; ++bd) {
+    const int64_t b = bd / dim, d = bd % dim;
+    double* h = (double*)malloc(sizeof(double) * 2 * (size_t)N);
+    for (int64_t i = 0; i < 2 * N; ++i) h[i] = h0 ? h0[bd * 2 * N + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      const double xv = x[bd * L + t];
+      double yv;
+      cstep(N, disc, use_softplus, xv, dt[bd * L + t], dt_bias ? dt_bias[d] : 0.0, A + d * 2 * N,
+            B + (b * N * L + t) * 2, 2 * L, C + (b * N * L + t) * 2, h, &yv);
+      if (Dskip) yv += Dskip[d] * xv;
+      if (z) {
+        const double zv = z[bd * L + t];
+        yv *= zv / (1.0 + exp(-zv));
+      }
+      y[bd * L + t] = yv;
+    }
+    if (h_final)
+      for (int64_t i = 0; i < 2 * N; ++i) h_final[bd * 2 * N + i] = h[i];
+    free(h);
+  }
+  return 0;
+}
+
+/* One decode step of oracle_complex_scan_f64; state [batch][dim][dstate][2] updated in place; x, dt, z, y [batch][dim];
+ * B, C [batch][dstate][2]. */
+int oracle_complex_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, int disc, int use_softplus,
+                                    double* state, const double* x, const double* dt, const double* dt_bias,
+                                    const double* A, const double* B, const double* C, const double* Dskip,
+                                    const double* z, double* y) {
+  if (batch < 0 || dim < 0 || dstate < 1) return 1;
+  if (!state || !x || !dt || !A || !B || !C || !y) return 2;
+  const int64_t N = dstate;
+  for (int64_t bd = 0; bd < batch * dim; ++bd) {
+    const int64_t b = bd / dim, d = bd % dim;
+    double yv;
+    cstep(N, disc, use_softplus, x[bd], dt[bd], dt_bias ? dt_bias[d] : 0.0, A + d * 2 * N, B + b * N * 2, 2,
+          C + b * N * 2, state + bd * 2 * N, &yv);
+    if (Dskip) yv += Dskip[d] * x[bd];
+    if (z) yv *= z[bd] / (1.0 + exp(-z[bd]));
+    y[bd] = yv;
+  }
+  return 0;
+}
+

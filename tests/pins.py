@@ -368,6 +368,68 @@ def pin_conv_split(orc, seed=12):
     assert np.array_equal(s3, np.concatenate([st[:, :, 1:], x[:, :, :1]], axis=2)), "P12 short"
 
 
+# P13: complex diagonal A (Mamba paper section 3.6, S4D-Lin).  (a) real inputs reduce to the (pinned) real oracle,
+#      both rules; (b) LTI case = convolution with K_k = Re(sum_n C_n Abar_n^k Bbar_n) built from numpy complex powers
+#      (brute force), both rules; (c) conjugating A, B, C, h0 leaves y unchanged and conjugates h_final; (d) an
+#      impulse through a pure rotation (A = i w, N = 1, Delta = dt fixed): y_t = Delta cos(w Delta t); (e) L decode
+#      steps = one scan.
+def pin_complex(orc, seed=13):
+    r = _rng(seed)
+    b, D, L, N = 2, 3, 24, 4
+    x = r.standard_normal((b, D, L))
+    dt = r.uniform(-3.0, 0.5, (b, D, L))
+    bias = r.uniform(-0.5, 0.5, D)
+    Are = -r.uniform(0.3, 2.0, (D, N))
+    Aim = r.uniform(-4.0, 4.0, (D, N))
+    Bre, Bim = r.standard_normal((b, N, L)), r.standard_normal((b, N, L))
+    Cre, Cim = r.standard_normal((b, N, L)), r.standard_normal((b, N, L))
+    Dk = r.standard_normal(D)
+    z = r.standard_normal((b, D, L))
+    h0 = r.standard_normal((b, D, N)) + 1j * r.standard_normal((b, D, N))
+    for disc in (EULER_B, ZOH):
+        # (a)
+        y1, h1 = orc.scan(x, dt, Are, Bre, Cre, dt_bias=bias, Dskip=Dk, z=z, h0=h0.real, disc=disc)
+        y2, h2 = orc.complex_scan(x, dt, Are + 0j, Bre + 0j, Cre + 0j, dt_bias=bias, Dskip=Dk, z=z, h0=h0.real + 0j,
+                                  disc=disc)
+        assert np.max(np.abs(y1 - y2)) < 1e-12 and np.max(np.abs(h1 - h2)) < 1e-12, ("P13a", disc)
+        # (b) LTI: constant Delta per channel, constant B, C
+        A = Are + 1j * Aim
+        Bc = (Bre[:, :, :1] + 1j * Bim[:, :, :1]) * np.ones((1, 1, L))
+        Cc = (Cre[:, :, :1] + 1j * Cim[:, :, :1]) * np.ones((1, 1, L))
+        dtc = np.repeat(dt[:, :, :1], L, axis=2)
+        y, _ = orc.complex_scan(x, dtc, A, Bc, Cc, Dskip=Dk, disc=disc)
+        for bi in range(b):
+            for d in range(D):
+                delta = np.log1p(np.exp(dtc[bi, d, 0]))
+                ab = np.exp(delta * A[d])
+                coef = delta if disc == EULER_B else (ab - 1.0) / A[d]
+                bb = coef * Bc[bi, :, 0]
+                K = np.array([np.sum(Cc[bi, :, 0] * ab ** k * bb).real for k in range(L)])
+                ref = np.array([np.sum(K[:t + 1][::-1] * x[bi, d, :t + 1]) for t in range(L)]) + Dk[d] * x[bi, d]
+                assert np.max(np.abs(ref - y[bi, d])) < 1e-10, ("P13b", disc)
+        # (c)
+        B = Bre + 1j * Bim
+        C = Cre + 1j * Cim
+        ya, ha = orc.complex_scan(x, dt, A, B, C, dt_bias=bias, Dskip=Dk, z=z, h0=h0, disc=disc)
+        yb, hb = orc.complex_scan(x, dt, A.conj(), B.conj(), C.conj(), dt_bias=bias, Dskip=Dk, z=z, h0=h0.conj(),
+                                  disc=disc)
+        assert np.max(np.abs(ya - yb)) < 1e-12 and np.max(np.abs(ha - hb.conj())) < 1e-12, ("P13c", disc)
+        # (e)
+        st = h0.copy()
+        for t in range(L):
+            yd, st = orc.complex_state_update(st, x[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], dt_bias=bias,
+                                              Dskip=Dk, z=z[:, :, t], disc=disc)
+            assert np.max(np.abs(yd - ya[:, :, t])) < 1e-12, ("P13e", disc, t)
+        assert np.max(np.abs(st - ha)) < 1e-12, ("P13e state", disc)
+    # (d)
+    w, delta, T = 0.7, 0.3, 40
+    xi = np.zeros((1, 1, T))
+    xi[0, 0, 0] = 1.0
+    y, _ = orc.complex_scan(xi, np.full((1, 1, T), delta), np.array([[1j * w]]), np.ones((1, 1, T)) + 0j,
+                            np.ones((1, 1, T)) + 0j, softplus=False)
+    assert np.max(np.abs(y[0, 0] - delta * np.cos(w * delta * np.arange(T)))) < 1e-13, "P13d"
+
+
 def all_pins(orc, worked_rows):
     """Run every pin; returns a list of (name, error-or-None)."""
     out = []
@@ -383,7 +445,8 @@ def all_pins(orc, worked_rows):
                    ("reset_hold_%d" % disc, lambda disc=disc: pin_reset_hold(orc, disc)),
                    ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
                    ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
-    out += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc))]
+    out += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
+            ("complex", lambda: pin_complex(orc))]
     for name, fn in checks:
         try:
             fn()

@@ -85,6 +85,10 @@ def test_conv_split(orc):
     pins.pin_conv_split(orc)
 
 
+def test_complex_a(orc):
+    pins.pin_complex(orc)
+
+
 def test_softplus_tails(orc):
     # Delta for very negative / positive logits: log1p(e^u) ~ e^u and ~ u + e^-u (no cancellation, no overflow).
     u = np.array([-40.0, -12.0, 0.0, 12.0, 40.0, 700.0])
@@ -132,6 +136,10 @@ MUTANTS = [
     ("conv_bias_dropped", r"double acc = bias \? bias\[d\] : 0\.0;", "double acc = 0.0;"),
     ("conv_state_out_shift", r"const int64_t tau = seqlen - S \+ i;", "const int64_t tau = seqlen - S + i - 1;"),
     ("conv_sigmoid_not_silu", r"use_silu \? acc / \(1\.0 \+ exp\(-acc\)\)", "use_silu ? 1.0 / (1.0 + exp(-acc))"),
+    ("complex_rotation_sign", r"h\[2 \* n \+ 1\] = abr \* hi \+ abi \* hr \+ bbi;", "h[2 * n + 1] = abr * hi - abi * hr + bbi;"),
+    ("complex_output_sign", r"y \+= Ct\[n \* bstride\] \* h\[2 \* n\] - Ct", "y += Ct[n * bstride] * h[2 * n] + Ct"),
+    ("complex_zoh_division", r"ci = \(ei \* ar - er \* ai\) / den;", "ci = (ei * ar + er * ai) / den;"),
+    ("complex_cos_sin_swapped", r"abr = mag \* cos\(ang\), abi = mag \* sin\(ang\)", "abr = mag * sin(ang), abi = mag * cos(ang)"),
 ]
 
 
