@@ -44,6 +44,13 @@ def scan_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
     return 2.0 * per_elem * b * D * L
 
 
+def complex_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
+    """Complex-A forward per (b, d, t) in FMA-slot units x 2: per state Delta*Re(A), exp (2), sin + cos (4),
+    (Delta x) B (2), the complex update (4), Re(C h) (2) and its sum (1) = 16; per element as the real scan (25)."""
+    per_elem = 16 * N + 1 + 11 + 1 + (1 if dskip else 0) + (7 if gate else 0)
+    return 2.0 * per_elem * b * D * L
+
+
 def conv_algorithmic_flops(b, D, L, width=4):
     """The causal convolution + SiLU in front of the scan, per (b, d, t): width FMAs, SiLU = exp + rcp (4 slots) + 2."""
     return 2.0 * (width + 6) * b * D * L
@@ -120,6 +127,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-complex", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (torch) five times: the reference kernel "
@@ -247,6 +255,39 @@ def main():
                             "algorithmic_bytes": nbytes + D * 4 * 5,
                             "note": "x is read once and the convolved sequence never goes to memory; a separate "
                                     "convolution kernel would add a write and a read of it (2 x 168 MB in bf16)"}
+
+    # ---- complex diagonal A (S4D-Lin) on the same shape: complex B, C and state
+    if not args.no_complex:
+        from selective_state_space_57_amd import _abi
+        hc = I.complex_inputs(w)
+        A2, B2, C2 = up(hc["A"]), up(hc["B"]), up(hc["C"])
+        hfc = torch.empty((b, D, N, 2), dtype=torch.float32, device=dev)
+        xargs = (d["x"].data_ptr(), d["dt"].data_ptr(), d["dt_bias"].data_ptr(), A2.data_ptr(), B2.data_ptr(),
+                 C2.data_ptr(), d["Dskip"].data_ptr(), d["z"].data_ptr(), 0, y.data_ptr(), hfc.data_ptr(),
+                 stream.cuda_stream)
+
+        def xstep():
+            st = _abi.complex_scan_fwd_raw(p, *xargs)
+            if st:
+                _abi.check(st)
+
+        for _ in range(3):
+            xstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nx = max(1, args.steps // 4)
+        e0.record(stream)
+        for _ in range(nx):
+            xstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        xms = e0.elapsed_time(e1) / nx
+        xfl = complex_algorithmic_flops(b, D, L, N)
+        out["complex_scan"] = {"workload": "mamba2.8b-layer shape, complex diagonal A (S4D-Lin), complex B, C",
+                               "ms_per_step": xms, "elements_per_s": elems / (xms * 1e-3),
+                               "ratio_to_real_scan": xms / ms, "algorithmic_flops": xfl,
+                               "achieved_TFLOPs": xfl / (xms * 1e-3) / 1e12,
+                               "frac_of_valu_peak": xfl / (xms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS}
 
     # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
     if not args.no_bwd:

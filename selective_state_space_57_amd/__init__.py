@@ -2,7 +2,8 @@
 
 ``scan_fwd``, ``scan_bwd`` and ``state_update`` call the C ABI of libssm57.so (include/ssm_scan.h) on PyTorch device
 tensors; ``conv_scan_fwd`` and ``conv_state_update`` do the same with the block's causal depthwise convolution + SiLU
-applied to x inside the kernels.  The arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded
+applied to x inside the kernels; ``complex_scan_fwd`` and ``complex_state_update`` run the complex-A variant.  The
+arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded
 synthetic workloads.
 """
 from __future__ import annotations
@@ -11,7 +12,8 @@ from . import _abi
 from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_params, workspace_bytes, plan_segments,
                    bwd_workspace_bytes)
 
-__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "EULER_B", "ZOH", "SSMError",
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "complex_scan_fwd",
+           "complex_state_update", "EULER_B", "ZOH", "SSMError",
            "Params", "make_params", "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
@@ -227,6 +229,60 @@ def conv_state_update(state, conv_state, x, conv_w, dt, A, B, C, dt_bias=None, D
         y = torch.empty((b, D), dtype=ydt, device=dev)
     st = _abi.conv_state_update_raw(p, cp, _addr(state), _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B),
                                     _addr(C), _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, dev))
+    _abi.check(st)
+    return y
+
+
+def complex_scan_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=None, h_final=None,
+                     y_dtype=None, disc=EULER_B, softplus=True, return_final_state=True, stream=None):
+    """Complex diagonal A: A (D, N, 2) float32 and B, C (b, N, L, 2) in x's dtype hold (re, im) pairs; h0 / h_final
+    (b, D, N, 2) float32.  y = Re(sum C h) + D x, gated.  Returns (y, h_final)."""
+    import torch
+    b, D, L = x.shape
+    N = A.shape[1]
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("x", x, (b, D, L), x.dtype, False), ("dt", dt, (b, D, L), x.dtype, False),
+                                   ("z", z, (b, D, L), x.dtype, True), ("B", B, (b, N, L, 2), x.dtype, False),
+                                   ("C", C, (b, N, L, 2), x.dtype, False), ("A", A, (D, N, 2), f32, False),
+                                   ("dt_bias", dt_bias, (D,), f32, True), ("Dskip", Dskip, (D,), f32, True),
+                                   ("h0", h0, (b, D, N, 2), f32, True), ("y", y, (b, D, L), ydt, True),
+                                   ("h_final", h_final, (b, D, N, 2), f32, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    p = make_params(b, D, L, N, io, io_code(ydt), disc, softplus, 0)
+    if y is None:
+        y = torch.empty((b, D, L), dtype=ydt, device=dev)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((b, D, N, 2), dtype=f32, device=dev)
+    st = _abi.complex_scan_fwd_raw(p, _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C),
+                                   _addr(Dskip), _addr(z), _addr(h0), _addr(y), _addr(h_final),
+                                   _stream_handle(stream, dev))
+    _abi.check(st)
+    return y, h_final
+
+
+def complex_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=None, y_dtype=None,
+                         disc=EULER_B, softplus=True, stream=None):
+    """One complex decode step: state (b, D, N, 2) float32 in place; x, dt, z (b, D); B, C (b, N, 2).  Returns y."""
+    import torch
+    b, D, N = state.shape[:3]
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("state", state, (b, D, N, 2), f32, False), ("x", x, (b, D), x.dtype, False),
+                                   ("dt", dt, (b, D), x.dtype, False), ("z", z, (b, D), x.dtype, True),
+                                   ("B", B, (b, N, 2), x.dtype, False), ("C", C, (b, N, 2), x.dtype, False),
+                                   ("A", A, (D, N, 2), f32, False), ("dt_bias", dt_bias, (D,), f32, True),
+                                   ("Dskip", Dskip, (D,), f32, True), ("y", y, (b, D), ydt, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    p = make_params(b, D, 1, N, io, io_code(ydt), disc, softplus, 0)
+    if y is None:
+        y = torch.empty((b, D), dtype=ydt, device=dev)
+    st = _abi.complex_state_update_raw(p, _addr(state), _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B),
+                                       _addr(C), _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, dev))
     _abi.check(st)
     return y
 

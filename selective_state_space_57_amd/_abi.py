@@ -17,7 +17,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE"
           5: "SSM_ERR_ALIGN", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_HIP"}
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
            "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
-           "ssm_conv_scan_fwd", "ssm_conv_state_update"]
+           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update"]
 
 
 class Params(ctypes.Structure):
@@ -69,6 +69,10 @@ def lib():
         L.ssm_conv_scan_fwd.restype = ctypes.c_int
         L.ssm_conv_state_update.argtypes = [PP, CP] + [P] * 11
         L.ssm_conv_state_update.restype = ctypes.c_int
+        L.ssm_complex_scan_fwd.argtypes = [PP] + [P] * 12
+        L.ssm_complex_scan_fwd.restype = ctypes.c_int
+        L.ssm_complex_state_update.argtypes = [PP] + [P] * 11
+        L.ssm_complex_state_update.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -117,6 +121,14 @@ def conv_scan_fwd_raw(p: Params, conv: ConvParams, x, dt, dt_bias, A, B, C, Dski
 def conv_state_update_raw(p: Params, conv: ConvParams, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):
     return lib().ssm_conv_state_update(ctypes.byref(p), ctypes.byref(conv), state, x, dt, dt_bias, A, B, C, Dskip, z,
                                        y, stream)
+
+
+def complex_scan_fwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream):
+    return lib().ssm_complex_scan_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream)
+
+
+def complex_state_update_raw(p: Params, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):
+    return lib().ssm_complex_state_update(ctypes.byref(p), state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream)
 
 
 def bwd_workspace_bytes(p: Params) -> int:

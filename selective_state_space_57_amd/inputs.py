@@ -15,7 +15,9 @@ Recipe (also written out in the design doc):
   * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state, 9 dy, 10 dh_final
     (the cotangents fed to the backward pass), 11 conv weight, 12 conv bias, 13 conv state (the causal convolution
     in front of the scan: weight and bias U(-1/sqrt(width), 1/sqrt(width)), the default init of a 1-D convolution
-    with one input channel per group; state N(0, 1));
+    with one input channel per group; state N(0, 1)), 14 imaginary part of B, 15 imaginary part of C, 16 imaginary
+    part of h0 and 17 the jitter of A's imaginary part (the complex-A variant; A is S4D-Lin, A_n = -1/2 + n i, with
+    the same N(0, a_jitter) jitter on both parts);
   * normals are numpy float32 standard normals; log-uniforms are exp(uniform(log lo, log hi)) in float64;
   * Delta-logit = softplus^-1(Delta*) - bias[d], with softplus^-1(v) = log(expm1(v)), rounded to the io dtype;
   * bf16 values are rounded to nearest-even from float32 (float64 -> float32 -> bf16 for float64 sources).
@@ -253,6 +255,40 @@ def random_small_conv(seed: int, b: int, D: int, N: int, width: int = 4, with_st
     """Convolution parameters matching random_small(seed, ...)."""
     w = Workload("small", b, D, 1, N, F32, 1e-3, 1e-1, 0.0, cfg_id=1000 + seed)
     return conv_params(w, width, with_state)
+
+
+def complex_inputs(w: Workload, step: int = 0, with_h0: bool = False) -> dict:
+    """Inputs of the complex-A scan: x, dt, z, dt_bias, Dskip as scan_inputs; A (D, N, 2) f32 S4D-Lin; B, C
+    (b, N, L, 2) in storage dtype (real parts = scan_inputs' B, C); h0 (b, D, N, 2) f32 or None.  Decode workloads
+    drop the seqlen axis as in scan_inputs."""
+    d = scan_inputs(w, step, with_h0=False)
+    b, D, N = w.batch, w.dim, w.dstate
+    L = 1 if w.decode_steps else w.seqlen
+    c, io = w.cfg_id, w.io
+    nbc = b * N * L
+    re = -0.5 + (_normal(c, 0, 3, D * N).astype(np.float64).reshape(D, N) * w.a_jitter if w.a_jitter > 0 else 0.0)
+    im = np.arange(N, dtype=np.float64)[None, :] + (
+        _normal(c, 0, 17, D * N).astype(np.float64).reshape(D, N) * w.a_jitter if w.a_jitter > 0 else 0.0)
+    A = np.stack([np.minimum(re, -1e-4) * np.ones((D, N)), im * np.ones((D, N))], axis=-1).astype(np.float32)
+    bshp = (b, N) if w.decode_steps else (b, N, L)
+    Bi = _normal_storage(c, step, 14, nbc, io).reshape(bshp)
+    Ci = _normal_storage(c, step, 15, nbc, io).reshape(bshp)
+    d["A"] = A
+    d["B"] = np.ascontiguousarray(np.stack([d["B"], Bi], axis=-1))
+    d["C"] = np.ascontiguousarray(np.stack([d["C"], Ci], axis=-1))
+    if with_h0:
+        d["h0"] = np.stack([_normal(c, 0, 8, b * D * N).reshape(b, D, N), _normal(c, 0, 16, b * D * N).reshape(b, D, N)],
+                           axis=-1).astype(np.float32)
+    return d
+
+
+def complex_as_oracle(d: dict) -> dict:
+    """Storage dict of complex_inputs -> oracle arguments (float64 / complex128)."""
+    f = {k: (None if v is None else to_f64(v)) for k, v in d.items()}
+    for k in ("A", "B", "C", "h0"):
+        if f.get(k) is not None:
+            f[k] = f[k][..., 0] + 1j * f[k][..., 1]
+    return f
 
 
 def decode_state(w: Workload) -> np.ndarray:
