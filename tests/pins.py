@@ -445,8 +445,8 @@ def all_pins(orc, worked_rows):
                    ("reset_hold_%d" % disc, lambda disc=disc: pin_reset_hold(orc, disc)),
                    ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
                    ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
-    out += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
-            ("complex", lambda: pin_complex(orc))]
+    checks += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
+               ("complex", lambda: pin_complex(orc))]
     for name, fn in checks:
         try:
             fn()

@@ -101,6 +101,16 @@ def test_softplus_tails(orc):
         assert abs(y[0, 0, 0] - exp) <= 1e-15 * max(1.0, exp), (uu, y[0, 0, 0], exp)
 
 
+def test_all_pins_run_and_pass(orc):
+    """The mutation test below relies on all_pins: every entry must be (name, None) for the true oracle, and every
+    family of pins must be in it (a check that is listed but never run would make the mutation test vacuous)."""
+    res = pins.all_pins(orc, load_worked())
+    assert all(isinstance(k, str) and e is None for k, e in res), [r for r in res if r[1] is not None]
+    names = {k for k, _ in res}
+    for must in ("worked", "theorem1", "zoh_euler", "split_0", "bwd_fd_1", "conv_numpy", "conv_split", "complex"):
+        assert must in names, must
+
+
 # Mutation test: each planted mistake is a regex substitution on oracle_scan.c; every mutant must fail a pin.
 MUTANTS = [
     ("drop_dskip", r"if \(has_D\) y \+= Dv \* xv;", "if (has_D) y += 0.0 * xv;"),
