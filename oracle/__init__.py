@@ -13,7 +13,9 @@ Pins (tests/test_oracle_pins.py) tie it to closed forms: the LTI convolution ker
 cumulative-sum (materialised) form, tree scans with the associative combine, split-sequence hand-off, linearity,
 reset/hold limits, the ZOH-to-Euler ratio and decode == scan.  The backward (``scan_bwd``, the chain rule through
 that definition) is pinned by central finite differences of the forward, element by element, for both discretisations,
-including A = 0 and the small-|Delta A| series branch.
+including A = 0 and the small-|Delta A| series branch.  The Mamba-2 SSD layer (``ssd``, scalar A per head) is pinned
+by the S6 recurrence with the head's scalar repeated over the state, by the masked quadratic (attention-like) form
+built from cumulative sums, by split-sequence hand-off and by decode == scan.
 """
 from __future__ import annotations
 
@@ -59,6 +61,10 @@ def _bind(path: str):
     lib.oracle_complex_scan_f64.restype = I
     lib.oracle_complex_state_update_f64.argtypes = [I64, I64, I64, I, I] + [P] * 10
     lib.oracle_complex_state_update_f64.restype = I
+    lib.oracle_ssd_f64.argtypes = [I64] * 6 + [I, I] + [P] * 11 + [I]
+    lib.oracle_ssd_f64.restype = I
+    lib.oracle_ssd_state_update_f64.argtypes = [I64] * 5 + [I, I] + [P] * 10
+    lib.oracle_ssd_state_update_f64.restype = I
     return lib
 
 
@@ -242,6 +248,47 @@ def complex_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None
     return y, st[..., 0] + 1j * st[..., 1]
 
 
+def ssd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, disc=EULER_B, softplus=True, nthreads=0,
+        _lib_override=None):
+    """Mamba-2 SSD layer (scalar A per head).  x, z: (b, L, H, P); dt: (b, L, H); A, dt_bias, Dskip: (H,);
+    B, C: (b, L, G, N); h0: (b, H, P, N).  Returns (y (b, L, H, P), h_final (b, H, P, N)) as float64 arrays."""
+    x = _f64(x)
+    bsz, L, H, P = x.shape
+    B = _f64(B)
+    G, N = B.shape[2], B.shape[3]
+    B = _f64(B, (bsz, L, G, N))
+    C = _f64(C, (bsz, L, G, N))
+    dt = _f64(dt, (bsz, L, H))
+    A = _f64(A, (H,))
+    y = np.zeros((bsz, L, H, P))
+    hf = np.zeros((bsz, H, P, N))
+    rc = (_lib_override or _load()).oracle_ssd_f64(
+        bsz, L, H, P, G, N, int(disc), int(bool(softplus)), _ptr(x), _ptr(dt), _ptr(_f64(dt_bias, (H,))), _ptr(A),
+        _ptr(B), _ptr(C), _ptr(_f64(Dskip, (H,))), _ptr(_f64(z, (bsz, L, H, P))), _ptr(_f64(h0, (bsz, H, P, N))),
+        _ptr(y), _ptr(hf), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_ssd_f64 failed with code %d" % rc)
+    return y, hf
+
+
+def ssd_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, disc=EULER_B, softplus=True,
+                     _lib_override=None):
+    """One SSD decode step: state (b, H, P, N) (a copy is updated and returned); x, z: (b, H, P); dt: (b, H);
+    B, C: (b, G, N).  Returns (y (b, H, P), new_state)."""
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    bsz, H, P, N = st.shape
+    B = _f64(B)
+    G = B.shape[1]
+    y = np.zeros((bsz, H, P))
+    rc = (_lib_override or _load()).oracle_ssd_state_update_f64(
+        bsz, H, P, G, N, int(disc), int(bool(softplus)), _ptr(st), _ptr(_f64(x, (bsz, H, P))),
+        _ptr(_f64(dt, (bsz, H))), _ptr(_f64(dt_bias, (H,))), _ptr(_f64(A, (H,))), _ptr(_f64(B, (bsz, G, N))),
+        _ptr(_f64(C, (bsz, G, N))), _ptr(_f64(Dskip, (H,))), _ptr(_f64(z, (bsz, H, P))), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_ssd_state_update_f64 failed with code %d" % rc)
+    return y, st
+
+
 class Oracle:
     """The oracle bound to a specific compiled library (the default one, or a test-built variant)."""
 
@@ -265,6 +312,12 @@ class Oracle:
 
     def complex_state_update(self, *a, **k):
         return complex_state_update(*a, _lib_override=self._lib, **k)
+
+    def ssd(self, *a, **k):
+        return ssd(*a, _lib_override=self._lib, **k)
+
+    def ssd_state_update(self, *a, **k):
+        return ssd_state_update(*a, _lib_override=self._lib, **k)
 
 
 def compile_variant(src_text: str, out_path: str) -> str:

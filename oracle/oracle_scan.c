@@ -427,3 +427,103 @@ int oracle_complex_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, 
   return 0;
 }
 
+
+/*
+ * Mamba-2 / state space duality (SSD) layer: the same selective recurrence with the state matrix reduced to a scalar
+ * times the identity per head, and a head structure like multi-head attention (close reading, section on Mamba-2
+ * and SSD; tutorial, "Mamba-2 与结构化对偶性": larger states such as N = 128 or 256).  nheads heads of width headdim
+ * split the channels; head h reads B and C of group g = h / (nheads / ngroups).  Per batch b, head h, column p the
+ * state is a row S[0..N-1]:
+ *   u     = dt[b,t,h] + dt_bias[h];  Delta = softplus(u) (or u)
+ *   abar  = exp(Delta * A[h])                       (one scalar per head and step)
+ *   coef  = Delta (Euler rule)  or  expm1(Delta*A[h]) / A[h]  (zero-order hold; Delta when A[h] == 0)
+ *   S[n]  = abar * S[n] + coef * B[b,t,g,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] * S[n] + D[h] * x[b,t,h,p],  times silu(z[b,t,h,p]) when z is given
+ * This is the recurrent form.  Its dual, the masked quadratic form y = (L o C B^T)(coef x) with the decay mask
+ * L[t,s] = exp(A * (cum_t - cum_s)) for s <= t, is what the pins compare it against; it is not used here.
+ * Layouts (fp64, row-major): x, z, y: [batch][seqlen][nheads][headdim]; dt: [batch][seqlen][nheads];
+ * B, C: [batch][seqlen][ngroups][dstate]; A, dt_bias, D: [nheads]; h0, h_final and the decode state:
+ * [batch][nheads][headdim][dstate].
+ */
+int oracle_ssd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                   int disc, int use_softplus, const double* x, const double* dt, const double* dt_bias,
+                   const double* A, const double* B, const double* C, const double* Dskip, const double* z,
+                   const double* h0, double* y, double* h_final, int nthreads) {
+  if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 || dstate > 4096 ||
+      nheads % ngroups)
+    return 1;
+  if (!x || !dt || !A || !B || !C || !y) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t H = nheads, P = headdim, N = dstate, G = ngroups, hpg = nheads / ngroups;
+  const int64_t nch = batch * H * P;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ch = 0; ch < nch; ch++) {
+    const int64_t b = ch / (H * P), h = (ch / P) % H, p = ch % P, g = h / hpg;
+    double S[4096];
+    for (int64_t n = 0; n < N; n++) S[n] = h0 ? h0[ch * N + n] : 0.0;
+    const double Ah = A[h];
+    for (int64_t t = 0; t < seqlen; t++) {
+      const int64_t row = (b * seqlen + t) * H + h;          /* index of (b, t, h) */
+      const double xv = x[row * P + p];
+      const double u = dt[row] + (dt_bias ? dt_bias[h] : 0.0);
+      const double delta = use_softplus ? sp(u) : u;
+      const double abar = exp(delta * Ah);
+      const double coef = disc == 0 ? delta : (Ah == 0.0 ? delta : expm1(delta * Ah) / Ah);
+      const double* Bt = B + ((b * seqlen + t) * G + g) * N;
+      const double* Ct = C + ((b * seqlen + t) * G + g) * N;
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; n++) {
+        S[n] = abar * S[n] + coef * Bt[n] * xv;
+        acc += Ct[n] * S[n];
+      }
+      if (Dskip) acc += Dskip[h] * xv;
+      if (z) {
+        const double zv = z[row * P + p];
+        acc *= zv / (1.0 + exp(-zv));
+      }
+      y[row * P + p] = acc;
+    }
+    if (h_final)
+      for (int64_t n = 0; n < N; n++) h_final[ch * N + n] = S[n];
+  }
+  return 0;
+}
+
+/* One SSD decode step: state [batch][nheads][headdim][dstate] updated in place; x, z, y: [batch][nheads][headdim];
+ * dt: [batch][nheads]; B, C: [batch][ngroups][dstate].  The same body as oracle_ssd_f64 for a single t. */
+int oracle_ssd_state_update_f64(int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                                int disc, int use_softplus, double* state, const double* x, const double* dt,
+                                const double* dt_bias, const double* A, const double* B, const double* C,
+                                const double* Dskip, const double* z, double* y) {
+  if (batch < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 || nheads % ngroups) return 1;
+  if (!state || !x || !dt || !A || !B || !C || !y) return 2;
+  const int64_t H = nheads, P = headdim, N = dstate, G = ngroups, hpg = nheads / ngroups;
+  for (int64_t b = 0; b < batch; b++)
+    for (int64_t h = 0; h < H; h++) {
+      const int64_t g = h / hpg;
+      const double Ah = A[h];
+      const double u = dt[b * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+      const double delta = use_softplus ? sp(u) : u;
+      const double abar = exp(delta * Ah);
+      const double coef = disc == 0 ? delta : (Ah == 0.0 ? delta : expm1(delta * Ah) / Ah);
+      const double* Bt = B + (b * G + g) * N;
+      const double* Ct = C + (b * G + g) * N;
+      for (int64_t p = 0; p < P; p++) {
+        const int64_t i = (b * H + h) * P + p;
+        double* S = state + i * N;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; n++) {
+          S[n] = abar * S[n] + coef * Bt[n] * x[i];
+          acc += Ct[n] * S[n];
+        }
+        if (Dskip) acc += Dskip[h] * x[i];
+        if (z) acc *= z[i] / (1.0 + exp(-z[i]));
+        y[i] = acc;
+      }
+    }
+  return 0;
+}

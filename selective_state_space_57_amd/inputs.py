@@ -21,6 +21,11 @@ Recipe (also written out in the design doc):
   * normals are numpy float32 standard normals; log-uniforms are exp(uniform(log lo, log hi)) in float64;
   * Delta-logit = softplus^-1(Delta*) - bias[d], with softplus^-1(v) = log(expm1(v)), rounded to the io dtype;
   * bf16 values are rounded to nearest-even from float32 (float64 -> float32 -> bf16 for float64 sources).
+
+Mamba-2 SSD workloads (SSDWorkload: batch, seqlen, nheads H, headdim P, ngroups G, dstate N) use the same tensor
+order and seeding with their own workload ids: 0 x (b, L, H, P), 1 Delta* (b, L, H), 2 bias (H), 3 A (H): minus a
+log-uniform value in [1, 16] (the range S4D-Real's -(n+1) spans for N = 16, one scalar per head), 4 B and 5 C
+(b, L, G, N), 6 Dskip (H), 7 z (b, L, H, P), 8 h0 (b, H, P, N).  Delta-logit = softplus^-1(Delta*) - bias[h].
 """
 from __future__ import annotations
 
@@ -67,6 +72,40 @@ WORKLOADS = {
     2: Workload("mamba2.8b-layer", 4, 5120, 4096, 16, BF16, 1e-3, 1e-1, 0.1, cfg_id=2),
     3: Workload("million-length", 1, 512, 1 << 20, 16, BF16, 1e-4, 1e-1, 0.1, cfg_id=3),
     4: Workload("decode-b256-d5120", 256, 5120, 1, 16, BF16, 1e-3, 1e-1, 0.1, decode_steps=64, cfg_id=4),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class SSDWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    io: str
+    delta_lo: float
+    delta_hi: float
+    gate: bool = True
+    dskip: bool = True
+    decode_steps: int = 0
+    cfg_id: int = 100
+
+    @property
+    def elements(self) -> int:
+        """b * D * L with D = nheads * headdim channels (the same count as the S6 workloads)."""
+        return self.batch * self.nheads * self.headdim * self.seqlen
+
+    def replace(self, **kw) -> "SSDWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# Mamba-2 2.7B (close reading, Mamba-2 paragraph): d_model 2560, expand 2 -> 5120 channels = 80 heads of 64, N = 128,
+# one group; the layer is run at the same batch and length as the Mamba-2.8B S6 layer above.
+SSD_WORKLOADS = {
+    0: SSDWorkload("tiny-ssd", 1, 200, 4, 64, 1, 128, BF16, 1e-3, 1e-1, cfg_id=100),
+    1: SSDWorkload("mamba2-2.7b-layer", 4, 4096, 80, 64, 1, 128, BF16, 1e-3, 1e-1, cfg_id=101),
 }
 
 
@@ -304,6 +343,52 @@ def random_small(seed: int, b: int, D: int, L: int, N: int, io: str = F32, delta
     if not bias:
         # fold the bias into the logit so that the same Delta values are produced without a bias vector
         lg = to_f64(d["dt"]) + d["dt_bias"].astype(np.float64)[None, :, None]
+        d["dt"] = to_storage(lg, io)
+        d["dt_bias"] = None
+    return d
+
+
+def ssd_inputs(w: SSDWorkload, step: int = 0, with_h0: bool = False) -> dict:
+    """Inputs of the SSD layer as storage arrays: x, z (b, L, H, P); dt (b, L, H); B, C (b, L, G, N); A, dt_bias,
+    Dskip (H,) f32; h0 (b, H, P, N) f32 or None.  Decode workloads drop the L axis."""
+    b, H, P, G, N = w.batch, w.nheads, w.headdim, w.ngroups, w.dstate
+    L = 1 if w.decode_steps else w.seqlen
+    c, io = w.cfg_id, w.io
+    bias = _softplus_inv(_loguniform(c, 0, 2, H, w.delta_lo, w.delta_hi)).astype(np.float32)
+    A = (-_loguniform(c, 0, 3, H, 1.0, 16.0)).astype(np.float32)
+    nx = b * L * H * P
+    ndt = b * L * H
+    x = _normal_storage(c, step, 0, nx, io)
+    bias64 = bias.astype(np.float64)
+    dt = _storage_empty(ndt, io)
+
+    def fdt(i, s0, e):
+        v = _loguniform_chunk(c, step, 1, i, e - s0, w.delta_lo, w.delta_hi)
+        np.expm1(v, out=v)
+        np.log(v, out=v)
+        v -= bias64[np.arange(s0, e, dtype=np.int64) % H]
+        dt[s0:e] = to_storage(v, io)
+    _fill(ndt, fdt)
+    Bm = _normal_storage(c, step, 4, b * L * G * N, io)
+    Cm = _normal_storage(c, step, 5, b * L * G * N, io)
+    Dskip = _normal(c, 0, 6, H).astype(np.float32) if w.dskip else None
+    z = _normal_storage(c, step, 7, nx, io) if w.gate else None
+    pre = (b,) if w.decode_steps else (b, L)
+    out = {"x": x.reshape(pre + (H, P)), "dt": dt.reshape(pre + (H,)), "dt_bias": bias, "A": A,
+           "B": Bm.reshape(pre + (G, N)), "C": Cm.reshape(pre + (G, N)), "Dskip": Dskip,
+           "z": None if z is None else z.reshape(pre + (H, P)), "h0": None}
+    if with_h0:
+        out["h0"] = _normal(c, 0, 8, b * H * P * N).reshape(b, H, P, N)
+    return out
+
+
+def random_small_ssd(seed: int, b: int, L: int, H: int, P: int, G: int, N: int, io: str = BF16, gate=True,
+                     dskip=True, bias=True, h0=False, delta=(1e-3, 1e-1)) -> dict:
+    """Small random SSD case for parity sweeps (odd lengths, optional parts switched off)."""
+    w = SSDWorkload("small-ssd", b, L, H, P, G, N, io, delta[0], delta[1], gate, dskip, cfg_id=2000 + seed)
+    d = ssd_inputs(w, with_h0=h0)
+    if not bias:
+        lg = to_f64(d["dt"]) + d["dt_bias"].astype(np.float64)
         d["dt"] = to_storage(lg, io)
         d["dt_bias"] = None
     return d

@@ -430,6 +430,92 @@ def pin_complex(orc, seed=13):
     assert np.max(np.abs(y[0, 0] - delta * np.cos(w * delta * np.arange(T)))) < 1e-13, "P13d"
 
 
+def _ssd_case(seed, b=2, L=37, H=4, P=3, G=2, N=5):
+    r = _rng(seed)
+    x = r.standard_normal((b, L, H, P))
+    dt = r.uniform(-4.0, 1.0, (b, L, H))
+    bias = r.uniform(-0.5, 0.5, H)
+    A = -r.uniform(0.2, 3.0, H)
+    A[1] = 0.0                       # the A == 0 limit of the zero-order hold
+    B = r.standard_normal((b, L, G, N))
+    C = r.standard_normal((b, L, G, N))
+    Dk = r.standard_normal(H)
+    z = r.standard_normal((b, L, H, P))
+    h0 = r.standard_normal((b, H, P, N))
+    return dict(x=x, dt=dt, dt_bias=bias, A=A, B=B, C=C, Dskip=Dk, z=z, h0=h0)
+
+
+def _ssd_as_s6(orc, c, disc, g, hpg):
+    """The heads of group g as S6 channels d = (head, column): A repeated over the state, B and C of the group."""
+    b, L, H, P = c["x"].shape
+    N = c["B"].shape[3]
+    hs = slice(g * hpg, (g + 1) * hpg)
+    x = c["x"][:, :, hs, :].transpose(0, 2, 3, 1).reshape(b, hpg * P, L)
+    z = c["z"][:, :, hs, :].transpose(0, 2, 3, 1).reshape(b, hpg * P, L)
+    dt = np.repeat(c["dt"][:, :, hs].transpose(0, 2, 1), P, axis=1)
+    A = np.repeat(c["A"][hs], P)[:, None] * np.ones((1, N))
+    bias = np.repeat(c["dt_bias"][hs], P)
+    Dk = np.repeat(c["Dskip"][hs], P)
+    h0 = c["h0"][:, hs].reshape(b, hpg * P, N)
+    y, hf = orc.scan(x, dt, A, c["B"][:, :, g, :].transpose(0, 2, 1), c["C"][:, :, g, :].transpose(0, 2, 1),
+                     dt_bias=bias, Dskip=Dk, z=z, h0=h0, disc=disc)
+    return y.reshape(b, hpg, P, L).transpose(0, 3, 1, 2), hf.reshape(b, hpg, P, N)
+
+
+def pin_ssd(orc, seed=14):
+    """Mamba-2 SSD layer (close reading, section on Mamba-2/SSD; tutorial, "Mamba-2 与结构化对偶性"):
+    (a) it is the S6 recurrence with the head's scalar A on every state entry and the group's B, C;
+    (b) it equals the masked quadratic form y = (L o C B^T)(coef x) + D x with L[t,s] = exp(A (cum_t - cum_s)),
+        cum = cumulative sum of Delta, plus the h0 term exp(A cum_t) C_t h0^T, computed with cumulative sums and
+        one matrix product per head (the attention-like dual of the recurrence);
+    (c) a split sequence with the state handed over equals one pass; (d) decode steps equal the scan."""
+    c = _ssd_case(seed)
+    b, L, H, P = c["x"].shape
+    G, N = c["B"].shape[2], c["B"].shape[3]
+    hpg = H // G
+    for disc in (EULER_B, ZOH):
+        y, hf = orc.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], dt_bias=c["dt_bias"], Dskip=c["Dskip"], z=c["z"],
+                        h0=c["h0"], disc=disc)
+        # (a)
+        for g in range(G):
+            ys, hs = _ssd_as_s6(orc, c, disc, g, hpg)
+            assert np.max(np.abs(ys - y[:, :, g * hpg:(g + 1) * hpg])) < 1e-12, ("P14a y", disc, g)
+            assert np.max(np.abs(hs - hf[:, g * hpg:(g + 1) * hpg])) < 1e-12, ("P14a h", disc, g)
+        # (b)
+        delta = _softplus_lib(c["dt"] + c["dt_bias"][None, None, :])            # (b, L, H)
+        for bi in range(b):
+            for h in range(H):
+                a, g = c["A"][h], h // hpg
+                dl = delta[bi, :, h]
+                cum = np.cumsum(dl)
+                coef = _coef(dl, np.full(L, a), disc)
+                Lm = np.tril(np.exp(a * (cum[:, None] - cum[None, :])))
+                Bg, Cg = c["B"][bi, :, g, :], c["C"][bi, :, g, :]
+                xh = c["x"][bi, :, h, :]                                          # (L, P)
+                ssm = (Lm * (Cg @ Bg.T)) @ (coef[:, None] * xh) + np.exp(a * cum)[:, None] * (Cg @ c["h0"][bi, h].T)
+                ref = (ssm + c["Dskip"][h] * xh) * _silu(c["z"][bi, :, h, :])
+                assert _rel(y[bi, :, h, :], ref) < 1e-11, ("P14b y", disc, bi, h)
+                wts = np.exp(a * (cum[-1] - cum)) * coef
+                href = (xh * wts[:, None]).T @ Bg + np.exp(a * cum[-1]) * c["h0"][bi, h]
+                assert _rel(hf[bi, h], href) < 1e-11, ("P14b h", disc, bi, h)
+        # (c)
+        L1 = 15
+        part = {k: c[k] for k in ("dt_bias", "Dskip", "A")}
+        y1, h1 = orc.ssd(c["x"][:, :L1], c["dt"][:, :L1], B=c["B"][:, :L1], C=c["C"][:, :L1], z=c["z"][:, :L1],
+                         h0=c["h0"], disc=disc, **part)
+        y2, h2 = orc.ssd(c["x"][:, L1:], c["dt"][:, L1:], B=c["B"][:, L1:], C=c["C"][:, L1:], z=c["z"][:, L1:], h0=h1,
+                         disc=disc, **part)
+        assert np.max(np.abs(np.concatenate([y1, y2], axis=1) - y)) < 1e-12, ("P14c y", disc)
+        assert np.max(np.abs(h2 - hf)) < 1e-12, ("P14c h", disc)
+        # (d)
+        st = c["h0"]
+        for t in range(L):
+            yd, st = orc.ssd_state_update(st, c["x"][:, t], c["dt"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                                          dt_bias=c["dt_bias"], Dskip=c["Dskip"], z=c["z"][:, t], disc=disc)
+            assert np.max(np.abs(yd - y[:, t])) < 1e-12, ("P14d", disc, t)
+        assert np.max(np.abs(st - hf)) < 1e-12, ("P14d state", disc)
+
+
 def all_pins(orc, worked_rows):
     """Run every pin; returns a list of (name, error-or-None)."""
     out = []
@@ -446,7 +532,7 @@ def all_pins(orc, worked_rows):
                    ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
                    ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
     checks += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
-               ("complex", lambda: pin_complex(orc))]
+               ("complex", lambda: pin_complex(orc)), ("ssd", lambda: pin_ssd(orc))]
     for name, fn in checks:
         try:
             fn()

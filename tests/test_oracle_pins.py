@@ -89,6 +89,10 @@ def test_complex_a(orc):
     pins.pin_complex(orc)
 
 
+def test_ssd(orc):
+    pins.pin_ssd(orc)
+
+
 def test_softplus_tails(orc):
     # Delta for very negative / positive logits: log1p(e^u) ~ e^u and ~ u + e^-u (no cancellation, no overflow).
     u = np.array([-40.0, -12.0, 0.0, 12.0, 40.0, 700.0])
@@ -107,7 +111,8 @@ def test_all_pins_run_and_pass(orc):
     res = pins.all_pins(orc, load_worked())
     assert all(isinstance(k, str) and e is None for k, e in res), [r for r in res if r[1] is not None]
     names = {k for k, _ in res}
-    for must in ("worked", "theorem1", "zoh_euler", "split_0", "bwd_fd_1", "conv_numpy", "conv_split", "complex"):
+    for must in ("worked", "theorem1", "zoh_euler", "split_0", "bwd_fd_1", "conv_numpy", "conv_split", "complex",
+                 "ssd"):
         assert must in names, must
 
 
@@ -150,6 +155,18 @@ MUTANTS = [
     ("complex_output_sign", r"y \+= Ct\[n \* bstride\] \* h\[2 \* n\] - Ct", "y += Ct[n * bstride] * h[2 * n] + Ct"),
     ("complex_zoh_division", r"ci = \(ei \* ar - er \* ai\) / den;", "ci = (ei * ar + er * ai) / den;"),
     ("complex_cos_sin_swapped", r"abr = mag \* cos\(ang\), abi = mag \* sin\(ang\)", "abr = mag * sin(ang), abi = mag * cos(ang)"),
+    ("ssd_group_index", r"g = h / hpg", "g = h % G"),
+    ("ssd_abar_sign", r"const double abar = exp\(delta \* Ah\);", "const double abar = exp(-delta * Ah);"),
+    ("ssd_euler_no_delta", r"coef = disc == 0 \? delta :", "coef = disc == 0 ? 1.0 :"),
+    ("ssd_zoh_no_div", r"expm1\(delta \* Ah\) / Ah", "expm1(delta * Ah)"),
+    ("ssd_dskip_head", r"acc \+= Dskip\[h\] \* xv;", "acc += Dskip[0] * xv;"),
+    ("ssd_y_before_update", r"S\[n\] = abar \* S\[n\] \+ coef \* Bt\[n\] \* xv;\n        acc \+= Ct\[n\] \* S\[n\];",
+     "acc += Ct[n] * S[n];\n        S[n] = abar * S[n] + coef * Bt[n] * xv;"),
+    ("ssd_h0_ignored", r"S\[n\] = h0 \? h0\[ch \* N \+ n\] : 0\.0;", "S[n] = 0.0;"),
+    ("ssd_B_time_shift", r"const double\* Bt = B \+ \(\(b \* seqlen \+ t\)", "const double* Bt = B + ((b * seqlen + (t > 0 ? t - 1 : 0))"),
+    ("ssd_decode_bias", r"const double u = dt\[b \* H \+ h\] \+ \(dt_bias \? dt_bias\[h\] : 0\.0\);",
+     "const double u = dt[b * H + h];"),
+    ("ssd_x_head0", r"const double xv = x\[row \* P \+ p\];", "const double xv = x[(row - h) * P + p];"),
 ]
 
 
