@@ -189,6 +189,51 @@ ssm_status ssm_scan_bwd(const ssm_scan_params* p, const void* x, const void* dt,
                         float* dDskip, void* dz, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Mamba-2 state space duality (SSD) layer: the selective recurrence with the state matrix reduced to a scalar times
+ * the identity per head and a multi-head structure (alishangtian.com close reading, the paragraph on Mamba-2 and SSD;
+ * docs.ifdog.com tutorial, "Mamba-2 与结构化对偶性", which names states of 128 or 256).  Channels are split into
+ * nheads heads of headdim columns; head h uses group g = h / (nheads / ngroups) of B and C:
+ *   Delta_t = softplus(dt[b,t,h] + dt_bias[h])   (or dt + dt_bias when dt_softplus == 0)
+ *   S[p][n] <- exp(Delta_t A[h]) S[p][n] + phi_t B[b,t,g,n] x[b,t,h,p],
+ *              phi_t = Delta_t (SSM_DISC_EULER_B) or expm1(Delta_t A[h]) / A[h] (SSM_DISC_ZOH; A == 0 gives Delta_t)
+ *   y[b,t,h,p] = (sum_n C[b,t,g,n] S[p][n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+ * The forward evaluates it in 64-step chunks as the masked quadratic (attention-like) form inside a chunk plus the
+ * recurrence between chunks, on the bf16 matrix cores with fp32 accumulation and fp32 state.
+ */
+typedef struct {
+  int64_t batch;       /* b >= 1 */
+  int64_t seqlen;      /* L >= 1 (ignored by ssm_ssd_state_update) */
+  int64_t nheads;      /* H >= 1, a multiple of ngroups */
+  int64_t headdim;     /* P: must be 64 */
+  int64_t ngroups;     /* G >= 1 */
+  int64_t dstate;      /* N: 64, 128 or 256 */
+  int32_t io_dtype;    /* must be SSM_BF16 (x, dt, B, C, z) */
+  int32_t y_dtype;     /* SSM_BF16 or SSM_F32 */
+  int32_t disc;        /* ssm_disc */
+  int32_t dt_softplus; /* 1: Delta = softplus(dt + dt_bias); 0: Delta = dt + dt_bias */
+  int32_t reserved;    /* must be 0 */
+} ssm_ssd_params;
+
+/*
+ * SSD forward over full sequences.  Layouts (row-major, heads inside time, as the pages' (batch, length, channels)):
+ *   x, z [batch][seqlen][nheads][headdim] bf16 (z NULL = no gate);  dt [batch][seqlen][nheads] bf16;
+ *   B, C [batch][seqlen][ngroups][dstate] bf16;  A, dt_bias, Dskip [nheads] fp32 (dt_bias / Dskip NULL = 0 / none);
+ *   h0, h_final [batch][nheads][headdim][dstate] fp32 or NULL (h0 NULL = zeros; h_final may alias h0);
+ *   y [batch][seqlen][nheads][headdim] y_dtype.
+ * x, B, C, z, y, h0 and h_final must be 16-byte aligned.  No workspace.  Errors as for ssm_scan_fwd, plus
+ * SSM_ERR_DTYPE for io_dtype != SSM_BF16 and SSM_ERR_UNSUPPORTED for headdim != 64 or dstate not in {64, 128, 256}.
+ */
+ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z, const float* h0, void* y,
+                       float* h_final, void* stream);
+
+/* One SSD decode step: state [batch][nheads][headdim][dstate] fp32 (16-byte aligned) updated in place;
+ * x, z, y [batch][nheads][headdim];  dt [batch][nheads];  B, C [batch][ngroups][dstate] (8-byte aligned). */
+ssm_status ssm_ssd_state_update(const ssm_ssd_params* p, float* state, const void* x, const void* dt,
+                                const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
+                                const void* z, void* y, void* stream);
+
 /* Static description of a status code. */
 const char* ssm_status_str(ssm_status s);
 

@@ -2,7 +2,8 @@
 
 ``scan_fwd``, ``scan_bwd`` and ``state_update`` call the C ABI of libssm57.so (include/ssm_scan.h) on PyTorch device
 tensors; ``conv_scan_fwd`` and ``conv_state_update`` do the same with the block's causal depthwise convolution + SiLU
-applied to x inside the kernels; ``complex_scan_fwd`` and ``complex_state_update`` run the complex-A variant.  The
+applied to x inside the kernels; ``complex_scan_fwd`` and ``complex_state_update`` run the complex-A variant;
+``ssd_fwd`` and ``ssd_state_update`` run the Mamba-2 SSD layer (scalar A per head, bf16 matrix cores).  The
 arithmetic runs entirely in the HIP kernels.  ``inputs`` generates the seeded
 synthetic workloads.
 """
@@ -13,7 +14,7 @@ from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_param
                    bwd_workspace_bytes)
 
 __all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "complex_scan_fwd",
-           "complex_state_update", "EULER_B", "ZOH", "SSMError",
+           "complex_state_update", "ssd_fwd", "ssd_state_update", "EULER_B", "ZOH", "SSMError",
            "Params", "make_params", "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
@@ -311,5 +312,60 @@ def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=N
         y = torch.empty((b, D), dtype=ydt, device=x.device)
     st = _abi.state_update_raw(p, _addr(state), _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C),
                                _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, x.device))
+    _abi.check(st)
+    return y
+
+
+def ssd_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=None, h_final=None, y_dtype=None,
+            disc=EULER_B, softplus=True, return_final_state=True, stream=None):
+    """Mamba-2 SSD layer.  x, z (b, L, H, P) bfloat16; dt (b, L, H) bfloat16; B, C (b, L, G, N) bfloat16; A, dt_bias,
+    Dskip (H,) float32; h0 / h_final (b, H, P, N) float32.  Returns (y (b, L, H, P), h_final)."""
+    import torch
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("x", x, (b, L, H, P), x.dtype, False), ("dt", dt, (b, L, H), x.dtype, False),
+                                   ("z", z, (b, L, H, P), x.dtype, True), ("B", B, (b, L, G, N), x.dtype, False),
+                                   ("C", C, (b, L, G, N), x.dtype, False), ("A", A, (H,), f32, False),
+                                   ("dt_bias", dt_bias, (H,), f32, True), ("Dskip", Dskip, (H,), f32, True),
+                                   ("h0", h0, (b, H, P, N), f32, True), ("y", y, (b, L, H, P), ydt, True),
+                                   ("h_final", h_final, (b, H, P, N), f32, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    p = _abi.make_ssd_params(b, L, H, P, G, N, io, io_code(ydt), disc, softplus)
+    if y is None:
+        y = torch.empty((b, L, H, P), dtype=ydt, device=dev)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((b, H, P, N), dtype=f32, device=dev)
+    st = _abi.ssd_fwd_raw(p, _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C), _addr(Dskip),
+                          _addr(z), _addr(h0), _addr(y), _addr(h_final), _stream_handle(stream, dev))
+    _abi.check(st)
+    return y, h_final
+
+
+def ssd_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=None, y_dtype=None, disc=EULER_B,
+                     softplus=True, stream=None):
+    """One SSD decode step: state (b, H, P, N) float32 updated in place; x, z (b, H, P); dt (b, H); B, C (b, G, N).
+    Returns y (b, H, P)."""
+    import torch
+    b, H, P, N = state.shape
+    G = B.shape[1]
+    io = io_code(x.dtype)
+    ydt = _out_dtype(y, y_dtype, x.dtype)
+    dev = x.device
+    f32 = torch.float32
+    for name, t, shp, dtp, opt in (("state", state, (b, H, P, N), f32, False), ("x", x, (b, H, P), x.dtype, False),
+                                   ("dt", dt, (b, H), x.dtype, False), ("z", z, (b, H, P), x.dtype, True),
+                                   ("B", B, (b, G, N), x.dtype, False), ("C", C, (b, G, N), x.dtype, False),
+                                   ("A", A, (H,), f32, False), ("dt_bias", dt_bias, (H,), f32, True),
+                                   ("Dskip", Dskip, (H,), f32, True), ("y", y, (b, H, P), ydt, True)):
+        _expect(name, t, shp, dtp, dev, optional=opt)
+    p = _abi.make_ssd_params(b, 1, H, P, G, N, io, io_code(ydt), disc, softplus)
+    if y is None:
+        y = torch.empty((b, H, P), dtype=ydt, device=dev)
+    st = _abi.ssd_state_update_raw(p, _addr(state), _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B),
+                                   _addr(C), _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, dev))
     _abi.check(st)
     return y

@@ -17,7 +17,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE"
           5: "SSM_ERR_ALIGN", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_HIP"}
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
            "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
-           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update"]
+           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update",
+           "ssm_ssd_fwd", "ssm_ssd_state_update"]
 
 
 class Params(ctypes.Structure):
@@ -30,6 +31,13 @@ class Params(ctypes.Structure):
 class ConvParams(ctypes.Structure):
     _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("state_in", ctypes.c_void_p),
                 ("state_out", ctypes.c_void_p), ("width", ctypes.c_int32), ("activation", ctypes.c_int32)]
+
+
+class SsdParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
+                ("dt_softplus", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SSMError(RuntimeError):
@@ -73,6 +81,11 @@ def lib():
         L.ssm_complex_scan_fwd.restype = ctypes.c_int
         L.ssm_complex_state_update.argtypes = [PP] + [P] * 11
         L.ssm_complex_state_update.restype = ctypes.c_int
+        SP = ctypes.POINTER(SsdParams)
+        L.ssm_ssd_fwd.argtypes = [SP] + [P] * 12
+        L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_ssd_state_update.argtypes = [SP] + [P] * 11
+        L.ssm_ssd_state_update.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -86,6 +99,20 @@ def make_params(batch, dim, seqlen, dstate, io_dtype=SSM_BF16, y_dtype=None, dis
                 segments=0) -> Params:
     return Params(int(batch), int(dim), int(seqlen), int(dstate), int(io_dtype),
                   int(io_dtype if y_dtype is None else y_dtype), int(disc), int(bool(softplus)), int(segments), 0)
+
+
+def make_ssd_params(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype=SSM_BF16, y_dtype=None, disc=EULER_B,
+                    softplus=True) -> SsdParams:
+    return SsdParams(int(batch), int(seqlen), int(nheads), int(headdim), int(ngroups), int(dstate), int(io_dtype),
+                     int(io_dtype if y_dtype is None else y_dtype), int(disc), int(bool(softplus)), 0)
+
+
+def ssd_fwd_raw(p: SsdParams, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream):
+    return lib().ssm_ssd_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream)
+
+
+def ssd_state_update_raw(p: SsdParams, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):
+    return lib().ssm_ssd_state_update(ctypes.byref(p), state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream)
 
 
 def check(status: int):

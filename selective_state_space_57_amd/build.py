@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssm_scan.hip", "ssm_conv_scan.hip", "ssm_complex_scan.hip",
-                                                  "ssm_scan_bwd.hip")]
+                                                  "ssm_scan_bwd.hip", "ssm_ssd.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm57.so")
 ARCH = "gfx950"

@@ -157,3 +157,44 @@ def test_conv_decode_needs_window(lib):
     v = {k: FAKE for k in ["state", "x", "dt", "A", "B", "C", "y"]}
     assert _abi.conv_state_update_raw(P(), conv, *[v.get(k, 0) for k in names], 0) == 1
 
+
+
+def SP(**kw):
+    base = dict(batch=2, seqlen=100, nheads=4, headdim=64, ngroups=2, dstate=128, io_dtype=_abi.SSM_BF16,
+                y_dtype=_abi.SSM_F32)
+    base.update(kw)
+    return _abi.make_ssd_params(**base)
+
+
+def call_ssd(p, **ptrs):
+    names = ["x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "h0", "y", "h_final"]
+    v = {k: FAKE for k in ["x", "dt", "A", "B", "C", "y"]}
+    v.update(ptrs)
+    return _abi.ssd_fwd_raw(p, *[v.get(k, 0) for k in names], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2), (dict(headdim=32), 4),
+    (dict(dstate=16), 4), (dict(dstate=96), 4), (dict(io_dtype=_abi.SSM_F32), 3), (dict(y_dtype=7), 3),
+    (dict(disc=2), 4), (dict(softplus=True), 0),
+])
+def test_ssd_param_errors(lib, kw, code):
+    p = SP(**kw)
+    if code == 0:
+        return                              # the valid base case is not launched on the CPU
+    assert call_ssd(p) == code
+    assert lib.ssm_last_error().decode()
+
+
+def test_ssd_null_and_align(lib):
+    for k in ["x", "dt", "A", "B", "C", "y"]:
+        assert call_ssd(SP(), **{k: 0}) == 1, k
+    for k in ["x", "B", "C", "y"]:
+        assert call_ssd(SP(), **{k: FAKE + 8}) == 5, k
+    p = SP()
+    p.reserved = 1
+    assert call_ssd(p) == 4
+    names = ["state", "x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "y"]
+    v = {k: FAKE for k in ["state", "x", "dt", "A", "B", "C", "y"]}
+    assert _abi.ssd_state_update_raw(SP(dstate=32), *[v.get(k, 0) for k in names], 0) == 4
+    assert _abi.ssd_state_update_raw(SP(), *[0 if k == "state" else v.get(k, 0) for k in names], 0) == 1
