@@ -81,6 +81,22 @@ def decode_algorithmic_bytes(b, D, N, io_bytes=2, gate=True, dskip=True):
             + D * 4 * (2 if dskip else 1))
 
 
+def ssd_algorithmic_bytes(b, L, H, P, G, N, y_bytes=2, gate=True, h_final=True):
+    """SSD layer: x (and z) read and y written once, dt read, B and C read once per group, h_final written (fp32),
+    A / dt_bias / Dskip per head."""
+    seq = b * L * H * P
+    return (seq * 2 * (2 if gate else 1) + seq * y_bytes + b * L * H * 2 + 2 * b * L * G * N * 2
+            + (b * H * P * N * 4 if h_final else 0) + 3 * H * 4)
+
+
+def ssd_algorithmic_flops(b, L, H, P, G, N, Q=64):
+    """FLOPs of the chunked dual form (one multiply-add = 2): per batch, chunk and group C B^T (2 Q^2 N); per batch,
+    chunk and head the masked product M x over the lower triangle (Q (Q+1) P), C S_prev (2 Q N P) and the state
+    update (2 Q N P)."""
+    nc = -(-L // Q)
+    return b * nc * (G * 2 * Q * Q * N + H * (Q * (Q + 1) * P + 4 * Q * N * P))
+
+
 def src_hash():
     """Hash of every kernel source file: counter records taken on other sources are stale."""
     h = hashlib.sha256()
@@ -128,6 +144,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-complex", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (torch) five times: the reference kernel "
@@ -288,6 +305,52 @@ def main():
                                "ratio_to_real_scan": xms / ms, "algorithmic_flops": xfl,
                                "achieved_TFLOPs": xfl / (xms * 1e-3) / 1e12,
                                "frac_of_valu_peak": xfl / (xms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS}
+
+    # ---- Mamba-2 SSD layer (scalar A per head, N = 128) at the Mamba-2 2.7B layer shape, bf16 matrix cores
+    if not args.no_ssd:
+        from selective_state_space_57_amd import _abi
+        sw = I.SSD_WORKLOADS[1]
+        sb, sL, sH, sP, sG, sN = sw.batch, sw.seqlen, sw.nheads, sw.headdim, sw.ngroups, sw.dstate
+        hs = I.ssd_inputs(sw)
+        sd = {k: up(v) for k, v in hs.items()}
+        ys = torch.empty((sb, sL, sH, sP), dtype=torch.bfloat16, device=dev)
+        hfs = torch.empty((sb, sH, sP, sN), dtype=torch.float32, device=dev)
+        spar = _abi.make_ssd_params(sb, sL, sH, sP, sG, sN, ssm.SSM_BF16, ssm.SSM_BF16)
+        sargs = (sd["x"].data_ptr(), sd["dt"].data_ptr(), sd["dt_bias"].data_ptr(), sd["A"].data_ptr(),
+                 sd["B"].data_ptr(), sd["C"].data_ptr(), sd["Dskip"].data_ptr(), sd["z"].data_ptr(), 0,
+                 ys.data_ptr(), hfs.data_ptr(), stream.cuda_stream)
+
+        def sstep():
+            st = _abi.ssd_fwd_raw(spar, *sargs)
+            if st:
+                _abi.check(st)
+
+        for _ in range(5):
+            sstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            sstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / args.steps
+        sby = ssd_algorithmic_bytes(sb, sL, sH, sP, sG, sN)
+        sfl = ssd_algorithmic_flops(sb, sL, sH, sP, sG, sN)
+        sgbs = sby / (sms * 1e-3) / 1e9
+        stf = sfl / (sms * 1e-3) / 1e12
+        selem = sb * sL * sH * sP
+        out["ssd"] = {"workload": "mamba2-2.7b-layer: batch %d, seqlen %d, %d heads x %d, ngroups %d, d_state %d, "
+                                  "bf16 io, gate + D" % (sb, sL, sH, sP, sG, sN),
+                      "ms_per_step": sms, "elements_per_s": selem / (sms * 1e-3),
+                      "ratio_to_s6_scan_same_elements": sms / ms if selem == elems else None,
+                      "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": sgbs / HBM_PEAK_GBS, "traffic": measured_traffic("ssd_fwd_kernel "
+                                                                                            "mamba2-2.7b-layer"),
+                                   "kernel": "ssd_fwd_kernel<128,bf16,euler,gate,dskip>",
+                                   "algorithmic_bytes": sby},
+                      "mfma": {"algorithmic_flops": sfl, "achieved_TFLOPs": stf, "peak_bf16_TFLOPs": 2500.0,
+                               "frac": stf / 2500.0}}
 
     # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
     if not args.no_bwd:

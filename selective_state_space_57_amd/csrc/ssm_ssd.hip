@@ -42,20 +42,24 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int kQ = 64;         // chunk length (steps)
 constexpr int kP = 64;         // head width (columns per head)
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kSStride = kQ + 8;  // bf16 row stride of the s-contiguous LDS arrays (144 bytes)
-constexpr int kTiles = 10;        // lower-triangular 16x16 tiles of a 64x64 chunk
+constexpr int kTiles = 10;     // lower-triangular 16x16 tiles of a 64x64 chunk
 
+// LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), double-buffered, stored
+// with the 16-byte units of each row permuted (unit u of row r sits at u ^ f(r)) so that both the row-wise operand
+// reads (16 rows, one unit) and the transposing reads (4 rows, 2 units) hit distinct banks.  The global->LDS copy
+// applies the permutation by choosing, per lane, which global unit to fetch.
 template <int N>
 struct alignas(16) SsdLds {
-  static constexpr int kNStride = N + 8;  // bf16 row stride of the n-contiguous arrays
-  uint16_t Bn[kQ * kNStride];   // B[s][n]
-  uint16_t Cn[kQ * kNStride];   // C[t][n]
-  uint16_t Bs[N * kSStride];    // B^T[n][s]
-  uint16_t xs[kP * kSStride];   // x^T[p][s]
-  u2 M[kTiles][2][64];          // M tiles in accumulator layout: [tile][hi, lo][lane] -> 4 bf16
-  alignas(16) float ac[kQ];     // A log2(e) cum_s
-  float phi[kQ];                // phi_s
-  float w[kQ];                  // phi_s exp(A (cum_63 - cum_s))
+  uint16_t B[2][kQ * N];     // B[s][n], double-buffered
+  uint16_t X[2][kQ * kP];    // x[s][p], double-buffered
+  uint16_t C[kQ * N];        // C[t][n]: its readers are done before the second barrier of a chunk, when the next
+                             // chunk's copy is issued
+  u2 M[kTiles][2][64];       // M tiles in accumulator layout: [tile][hi, lo][lane] -> 4 bf16
+  struct alignas(16) Scal {  // per-step scalars, one private copy per wave
+    float ac[kQ];            // A log2(e) cum_s
+    float phi[kQ];           // phi_s
+    float w[kQ];             // phi_s exp(A (cum_63 - cum_s))
+  } sc[4];
 };
 
 struct SsdArgs {
@@ -78,11 +82,12 @@ struct SsdArgs {
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-__device__ __forceinline__ uint32_t bf_bits(float v) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)));  // round to nearest even
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (first value in the low half), one v_cvt_pk_bf16_f32 (round to nearest even)
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
 }
-// two fp32 -> packed bf16 pair (first value in the low half)
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return bf_bits(a) | (bf_bits(b) << 16); }
 // v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), for 4 values: hi and lo each as 4 packed bf16
 __device__ __forceinline__ void split4(float a, float b, float c, float d, u2& hi, u2& lo) {
   const uint32_t h0 = pack2(a, b), h1 = pack2(c, d);
@@ -95,8 +100,36 @@ __device__ __forceinline__ f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ const uint16_t* at(const uint16_t* base, int byte_off) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
 __device__ __forceinline__ u4 lds16(const uint16_t* p) { return *reinterpret_cast<const u4*>(p); }
 __device__ __forceinline__ u2 lds8(const uint16_t* p) { return *reinterpret_cast<const u2*>(p); }
+// transposing read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element i%4 of the 8-byte pieces
+// addressed by lanes 4q + i/4 (q = 0..3).  With lane j pointing at row k0 + j/4, columns 4(j%4)..+3 of a row-major
+// tile, lane i receives the tile's column i at rows k0 .. k0+3.
+__device__ __forceinline__ u2 tr16(const uint16_t* p) {
+  return __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p)));
+}
+
+// unit permutation of a swizzled row: f maps every 4 consecutive rows to distinct values of f >> 1 and every 16 (8)
+// consecutive rows to distinct values of f
+template <int U>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (U >= 16)
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  else
+    return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+// byte offset of 16-byte unit u of row r in a swizzled array with U units per row
+template <int U>
+__device__ __forceinline__ int soff(int r, int u) {
+  return (r * U + (u ^ swz<U>(r))) * 16;
+}
 
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
@@ -108,101 +141,29 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
   return v;
 }
 
-template <int N>
-struct Prefetch {
-  static constexpr int kBTasks = N / 64;   // (s pair, 8-column group) tasks of B per thread
-  static constexpr int kCVec = N / 32;     // 16-byte vectors of C per thread
-  u4 b0[kBTasks], b1[kBTasks];
-  u4 c[kCVec];
-  u4 x0, x1;
-  uint32_t dt;
-};
-
-// Global loads of chunk `ck` into registers.  Rows past the sequence read as zero (buffer range check).
-template <int N>
-__device__ __forceinline__ void load_chunk(Prefetch<N>& pf, int ck, int tid, __amdgpu_buffer_rsrc_t rx,
-                                           __amdgpu_buffer_rsrc_t rdt, __amdgpu_buffer_rsrc_t rB,
-                                           __amdgpu_buffer_rsrc_t rC, int h, int g, int H, int G, int64_t L) {
-  const int t0 = ck * kQ;
-  const int sp = tid & 31;
-  // B: task = (s pair sp, column group cg)
+// Global->LDS copies of chunk ck.  Each instruction moves 1 KB: lane i fills physical unit 64 k + i of the array.
+// Rows past the sequence read as zero (buffer range check).
+template <int U>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t rsrc, int wave, int lane, int t0,
+                                           int L, int row_elems, int col0) {
+  constexpr int kInstr = kQ * U / 64;
 #pragma unroll
-  for (int i = 0; i < Prefetch<N>::kBTasks; ++i) {
-    const int cg = (tid >> 5) + 8 * i;
-    const int s0 = t0 + 2 * sp;
-    const uint32_t o0 = s0 < L ? static_cast<uint32_t>(((int64_t(s0) * G + g) * N + 8 * cg) * 2) : kDropOffset;
-    const uint32_t o1 = s0 + 1 < L ? static_cast<uint32_t>(((int64_t(s0 + 1) * G + g) * N + 8 * cg) * 2)
-                                   : kDropOffset;
-    pf.b0[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rB, static_cast<int>(o0), 0, 0));
-    pf.b1[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rB, static_cast<int>(o1), 0, 0));
-  }
-  // C: vector v = (row, column group), column group fastest
-#pragma unroll
-  for (int i = 0; i < Prefetch<N>::kCVec; ++i) {
-    const int v = tid + kThreads * i;
-    const int row = v / (N / 8), cg = v % (N / 8);
-    const int t = t0 + row;
-    const uint32_t o = t < L ? static_cast<uint32_t>(((int64_t(t) * G + g) * N + 8 * cg) * 2) : kDropOffset;
-    pf.c[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rC, static_cast<int>(o), 0, 0));
-  }
-  // x: task = (s pair sp, 8-column group pg)
-  {
-    const int pg = tid >> 5;
-    const int s0 = t0 + 2 * sp;
-    const uint32_t o0 = s0 < L ? static_cast<uint32_t>(((int64_t(s0) * H + h) * kP + 8 * pg) * 2) : kDropOffset;
-    const uint32_t o1 = s0 + 1 < L ? static_cast<uint32_t>(((int64_t(s0 + 1) * H + h) * kP + 8 * pg) * 2)
-                                   : kDropOffset;
-    pf.x0 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>(o0), 0, 0));
-    pf.x1 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>(o1), 0, 0));
-  }
-  // dt: lane s of wave 0 (other waves load nothing)
-  {
-    const int t = t0 + tid;
-    const uint32_t o = (tid < kQ && t < L) ? static_cast<uint32_t>((int64_t(t) * H + h) * 2) : kDropOffset;
-    pf.dt = static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, static_cast<int>(o),
-                                                                                               0, 0)));
+  for (int i = 0; i < kInstr / 4; ++i) {
+    const int k = wave + 4 * i;
+    const int P = 64 * k + lane;
+    const int r = P / U, u = (P % U) ^ swz<U>(r);
+    const int t = t0 + r;
+    const uint32_t o = t < L ? static_cast<uint32_t>((int64_t(t) * row_elems + col0 + 8 * u) * 2) : kDropOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 512 * k), 16, static_cast<int>(o), 0, 0, 0);
   }
 }
 
-// the bf16 pair (r0 element j, r1 element j) for j = 2k (even) or 2k+1 (odd)
-__device__ __forceinline__ uint32_t pair_even(uint32_t r0, uint32_t r1) { return (r0 & 0xffffu) | (r1 << 16); }
-__device__ __forceinline__ uint32_t pair_odd(uint32_t r0, uint32_t r1) { return (r0 >> 16) | (r1 & 0xffff0000u); }
-
-template <int N>
-__device__ __forceinline__ void store_chunk(SsdLds<N>& S, const Prefetch<N>& pf, int tid) {
-  constexpr int NS = SsdLds<N>::kNStride;
-  const int sp = tid & 31;
-#pragma unroll
-  for (int i = 0; i < Prefetch<N>::kBTasks; ++i) {
-    const int cg = (tid >> 5) + 8 * i;
-    *reinterpret_cast<u4*>(&S.Bn[(2 * sp) * NS + 8 * cg]) = pf.b0[i];
-    *reinterpret_cast<u4*>(&S.Bn[(2 * sp + 1) * NS + 8 * cg]) = pf.b1[i];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *reinterpret_cast<uint32_t*>(&S.Bs[(8 * cg + 2 * k) * kSStride + 2 * sp]) = pair_even(pf.b0[i][k], pf.b1[i][k]);
-      *reinterpret_cast<uint32_t*>(&S.Bs[(8 * cg + 2 * k + 1) * kSStride + 2 * sp]) =
-          pair_odd(pf.b0[i][k], pf.b1[i][k]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < Prefetch<N>::kCVec; ++i) {
-    const int v = tid + kThreads * i;
-    const int row = v / (N / 8), cg = v % (N / 8);
-    *reinterpret_cast<u4*>(&S.Cn[row * NS + 8 * cg]) = pf.c[i];
-  }
-  {
-    const int pg = tid >> 5;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *reinterpret_cast<uint32_t*>(&S.xs[(8 * pg + 2 * k) * kSStride + 2 * sp]) = pair_even(pf.x0[k], pf.x1[k]);
-      *reinterpret_cast<uint32_t*>(&S.xs[(8 * pg + 2 * k + 1) * kSStride + 2 * sp]) = pair_odd(pf.x0[k], pf.x1[k]);
-    }
-  }
-}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 template <int N, typename TY, bool ZOH, bool GATE, bool DSKIP>
-__global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
-  constexpr int NS = SsdLds<N>::kNStride;
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N <= 128 ? 2 : 1)))
+ssd_fwd_kernel(SsdArgs a) {
+  constexpr int U = N / 8;
   constexpr int NB = N / 16;   // 16-row state tiles per wave
   constexpr int NK = N / 32;   // 32-deep k-steps over the state
   __shared__ SsdLds<N> S;
@@ -214,7 +175,7 @@ __global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / a.hpg;
-  const int64_t L = a.L;
+  const int L = static_cast<int>(a.L);   // < 2^31: checked on the host
 
   const int64_t xrow = int64_t(L) * a.H * kP;    // x / z / y elements per batch
   const int64_t bcrow = int64_t(L) * a.G * N;    // B / C elements per batch
@@ -229,29 +190,45 @@ __global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
   const float A2 = Ah * kLog2e;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const float Dh = DSKIP ? a.Dskip[h] : 0.0f;
-  const int pcol = wave * 16 + l16;   // this lane's head column in the state and the M x product
+  const int pcol = wave * 16 + l16;   // this lane's head column in the state and the x M product
   const int64_t srow = (int64_t(b) * a.H + h) * kP + pcol;   // row of h0 / h_final
+  // transposing reads: lane j of a 16-lane group points at row k0 + j/4, columns 4(j%4) .. +3 of a 16-column tile
+  const int trow = l16 >> 2, tcol = 4 * (l16 & 3);
 
   // state tiles: hT[nb][c] = S[p = pcol][n = 16 nb + 4 g4 + c]
+  // (no h0: a zero-length buffer, whose reads return 0)
+  const int64_t hcount = int64_t(gridDim.x) * kP * N;
+  const auto rh0 = make_rsrc(a.h0 ? a.h0 : a.A, a.h0 ? hcount : 0);
   f4 hT[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (a.h0)
-      hT[nb] = *reinterpret_cast<const f4*>(a.h0 + srow * N + 16 * nb + 4 * g4);
-    else
-      hT[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int nb = 0; nb < NB; ++nb)
+    hT[nb] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rh0, static_cast<int>((srow * N + 16 * nb + 4 * g4) * 4), 0, 0));
 
-  Prefetch<N> pf;
-  load_chunk<N>(pf, 0, tid, rx, rdt, rB, rC, h, g, a.H, a.G, L);
+  auto load_dt = [&](int ck) -> uint32_t {
+    const int t = ck * kQ + lane;
+    const uint32_t o = t < L ? static_cast<uint32_t>((int64_t(t) * a.H + h) * 2) : kDropOffset;
+    return static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, static_cast<int>(o),
+                                                                                            0, 0)));
+  };
+  const int grow = a.G * N, gcol = g * N;          // B / C: row stride and column offset of this group
+  const int xrow_e = a.H * kP, xcol = h * kP;      // x: row stride and column offset of this head
+  stage_rows<U>(S.B[0], rB, wave, lane, 0, L, grow, gcol);
+  stage_rows<U>(S.C, rC, wave, lane, 0, L, grow, gcol);
+  stage_rows<8>(S.X[0], rx, wave, lane, 0, L, xrow_e, xcol);
+  uint32_t dtw = load_dt(0);
+  auto& sc = S.sc[wave];
 
   for (int ck = 0; ck < a.nchunks; ++ck) {
     const int t0 = ck * kQ;
-    __syncthreads();                      // the previous chunk's readers are done with LDS
-    store_chunk<N>(S, pf, tid);
-    if (wave == 0) {
-      // per-step scalars: Delta, phi, running sum, decay weights
-      const float u = bf_lo(pf.dt) + bias;
+    const int cb = ck & 1;
+    const uint16_t* Bc = S.B[cb];
+    const uint16_t* Cc = S.C;
+    const uint16_t* Xc = S.X[cb];
+    wait_vm0();                             // this wave's copies of chunk ck (and its dt) have landed
+    {
+      // per-step scalars (every wave computes its own copy): Delta, phi, running sum, decay weights
+      const float u = bf_lo(dtw) + bias;
       float dl = a.softplus ? softplus(u) : u;
       dl = (t0 + lane < L) ? dl : 0.0f;
       float ph = dl;
@@ -262,24 +239,27 @@ __global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
       const float cum = wave_incl_scan(dl, lane);
       const float acv = cum * A2;
       const float ac63 = __shfl(acv, 63, 64);
-      S.ac[lane] = acv;
-      S.phi[lane] = ph;
-      S.w[lane] = ph * hw_exp2(ac63 - acv);
+      sc.ac[lane] = acv;
+      sc.phi[lane] = ph;
+      sc.w[lane] = ph * hw_exp2(ac63 - acv);
     }
-    if (ck + 1 < a.nchunks) load_chunk<N>(pf, ck + 1, tid, rx, rdt, rB, rC, h, g, a.H, a.G, L);
-    // x and z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
-    u2 xo[4], zo[4];
+    __syncthreads();                        // chunk ck is in LDS everywhere; chunk ck-1 is finished by every wave
+    if (ck + 1 < a.nchunks) {
+      stage_rows<U>(S.B[cb ^ 1], rB, wave, lane, t0 + kQ, L, grow, gcol);
+      stage_rows<8>(S.X[cb ^ 1], rx, wave, lane, t0 + kQ, L, xrow_e, xcol);
+      dtw = load_dt(ck + 1);
+    }
+    // z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
+    u2 zo[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int t = t0 + 16 * tb + l16;
       const uint32_t o = t < L ? static_cast<uint32_t>(((int64_t(t) * a.H + h) * kP + 16 * wave + 4 * g4) * 2)
                                : kDropOffset;
-      xo[tb] = DSKIP ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rx, static_cast<int>(o), 0, 0))
-                     : u2{0u, 0u};
       zo[tb] = GATE ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<int>(o), 0, 0))
                     : u2{0u, 0u};
     }
-    __syncthreads();                      // chunk data and scalars are in LDS
+    const float* sac = sc.ac;
 
     // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb
     for (int ti = wave; ti < kTiles; ti += 4) {
@@ -288,15 +268,15 @@ __global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const u4 aB = lds16(&S.Bn[(16 * sb + l16) * NS + 32 * kk + 8 * g4]);
-        const u4 bC = lds16(&S.Cn[(16 * tb + l16) * NS + 32 * kk + 8 * g4]);
+        const u4 aB = lds16(at(Bc, soff<U>(16 * sb + l16, 4 * kk + g4)));
+        const u4 bC = lds16(at(Cc, soff<U>(16 * tb + l16, 4 * kk + g4)));
         acc = mfma(aB, bC, acc);
       }
       // acc[c] = CB[t = 16 tb + l16][s = 16 sb + 4 g4 + c]
       const int t = 16 * tb + l16;
-      const float act = S.ac[t];
-      const f4 acs = *reinterpret_cast<const f4*>(&S.ac[16 * sb + 4 * g4]);
-      const f4 phs = *reinterpret_cast<const f4*>(&S.phi[16 * sb + 4 * g4]);
+      const float act = sac[t];
+      const f4 acs = *reinterpret_cast<const f4*>(&sac[16 * sb + 4 * g4]);
+      const f4 phs = *reinterpret_cast<const f4*>(&sc.phi[16 * sb + 4 * g4]);
       float m[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -320,80 +300,94 @@ __global__ void __launch_bounds__(kThreads) ssd_fwd_kernel(SsdArgs a) {
       split4(hT[2 * kn][0], hT[2 * kn][1], hT[2 * kn][2], hT[2 * kn][3], h0h, h0l);
       split4(hT[2 * kn + 1][0], hT[2 * kn + 1][1], hT[2 * kn + 1][2], hT[2 * kn + 1][3], h1h, h1l);
       const u4 hh = cat(h0h, h1h), hl = cat(h0l, h1l);
+      const int half = (g4 & 1) * 8;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const uint16_t* cr = &S.Cn[(16 * tb + l16) * NS + 32 * kn + 4 * g4];
-        const u2 c0 = lds8(cr), c1 = lds8(cr + 16);
+        const int t = 16 * tb + l16;
+        const u2 c0 = lds8(at(Cc, soff<U>(t, 4 * kn + (g4 >> 1)) + half));
+        const u2 c1 = lds8(at(Cc, soff<U>(t, 4 * kn + 2 + (g4 >> 1)) + half));
         const u4 bC = cat(c0, c1);
         acc[tb] = mfma(hh, bC, acc[tb]);
         acc[tb] = mfma(hl, bC, acc[tb]);
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float et = hw_exp2(S.ac[16 * tb + l16]);
-      acc[tb] *= et;
-    }
+    for (int tb = 0; tb < 4; ++tb) acc[tb] *= hw_exp2(sac[16 * tb + l16]);
 
     // ---- state update: S_next^T[n][p] = exp2(ac_63) S_prev^T[n][p] + sum_s B^T[n][s] (w_s x[s][p])
     {
-      const float achunk = hw_exp2(S.ac[kQ - 1]);
+      const float achunk = hw_exp2(sac[kQ - 1]);
+      const int xhalf = (tcol & 4) * 2;   // byte offset of columns 4(j%4).. inside their 16-byte unit
       u4 xh[2], xl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const u4 xv = lds16(&S.xs[pcol * kSStride + 32 * ks + 8 * g4]);
-        const f4 w0 = *reinterpret_cast<const f4*>(&S.w[32 * ks + 8 * g4]);
-        const f4 w1 = *reinterpret_cast<const f4*>(&S.w[32 * ks + 8 * g4 + 4]);
-        u2 ah, al, bh, bl;
-        split4(bf_lo(xv[0]) * w0[0], bf_hi(xv[0]) * w0[1], bf_lo(xv[1]) * w0[2], bf_hi(xv[1]) * w0[3], ah, al);
-        split4(bf_lo(xv[2]) * w1[0], bf_hi(xv[2]) * w1[1], bf_lo(xv[3]) * w1[2], bf_hi(xv[3]) * w1[3], bh, bl);
-        xh[ks] = cat(ah, bh);
-        xl[ks] = cat(al, bl);
+        u2 hp[2], lp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int k0 = 32 * ks + 8 * g4 + 4 * e;
+          const u2 xv = tr16(at(Xc, soff<8>(k0 + trow, (16 * wave + tcol) >> 3) + xhalf));
+          const f4 wv = *reinterpret_cast<const f4*>(&sc.w[k0]);
+          split4(bf_lo(xv[0]) * wv[0], bf_hi(xv[0]) * wv[1], bf_lo(xv[1]) * wv[2], bf_hi(xv[1]) * wv[3], hp[e],
+                 lp[e]);
+        }
+        xh[ks] = cat(hp[0], hp[1]);
+        xl[ks] = cat(lp[0], lp[1]);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f4 st = hT[nb] * achunk;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u4 aB = lds16(&S.Bs[(16 * nb + l16) * kSStride + 32 * ks + 8 * g4]);
+          const int k0 = 32 * ks + 8 * g4;
+          const int unit = (16 * nb + tcol) >> 3;
+          const u2 b0 = tr16(at(Bc, soff<U>(k0 + trow, unit) + xhalf));
+          const u2 b1 = tr16(at(Bc, soff<U>(k0 + 4 + trow, unit) + xhalf));
+          const u4 aB = cat(b0, b1);
           st = mfma(aB, xh[ks], st);
           st = mfma(aB, xl[ks], st);
         }
         hT[nb] = st;
       }
     }
-    __syncthreads();                      // M tiles are in LDS
+    __syncthreads();                        // M tiles are in LDS; every wave is done with C
+    if (ck + 1 < a.nchunks) stage_rows<U>(S.C, rC, wave, lane, t0 + kQ, L, grow, gcol);
 
     // ---- intra-chunk part: Y^T[p][t] += sum_{s <= t} x^T[p][s] M[t][s]
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    {
+      const int xhalf = (tcol & 4) * 2;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (32 * kk > 16 * tb + 15) continue;   // the whole k-step lies above the diagonal
         // k-set: s = 32 kk + 4 g4 + c (tile sb = 2kk) and 32 kk + 16 + 4 g4 + c (tile 2kk+1)
-        const uint16_t* xr = &S.xs[pcol * kSStride + 32 * kk + 4 * g4];
-        const u2 x0 = lds8(xr), x1 = lds8(xr + 16);
+        const int unit = (16 * wave + tcol) >> 3;
+        const u2 x0 = tr16(at(Xc, soff<8>(32 * kk + 4 * g4 + trow, unit) + xhalf));
+        const u2 x1 = tr16(at(Xc, soff<8>(32 * kk + 16 + 4 * g4 + trow, unit) + xhalf));
         const u4 ax = cat(x0, x1);
-        const int sb0 = 2 * kk, sb1 = 2 * kk + 1;
-        const int t0i = tb * (tb + 1) / 2;
-        const u2 zero = {0u, 0u};
-        const u2 h0v = S.M[t0i + sb0][0][lane];
-        const u2 l0v = S.M[t0i + sb0][1][lane];
-        const u2 h1v = sb1 <= tb ? S.M[t0i + sb1][0][lane] : zero;
-        const u2 l1v = sb1 <= tb ? S.M[t0i + sb1][1][lane] : zero;
-        acc[tb] = mfma(ax, cat(h0v, h1v), acc[tb]);
-        acc[tb] = mfma(ax, cat(l0v, l1v), acc[tb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          if (32 * kk > 16 * tb + 15) continue;   // the whole k-step lies above the diagonal
+          const int sb0 = 2 * kk, sb1 = 2 * kk + 1;
+          const int t0i = tb * (tb + 1) / 2;
+          const u2 zero = {0u, 0u};
+          const u2 h0v = S.M[t0i + sb0][0][lane];
+          const u2 l0v = S.M[t0i + sb0][1][lane];
+          const u2 h1v = sb1 <= tb ? S.M[t0i + sb1][0][lane] : zero;
+          const u2 l1v = sb1 <= tb ? S.M[t0i + sb1][1][lane] : zero;
+          acc[tb] = mfma(ax, cat(h0v, h1v), acc[tb]);
+          acc[tb] = mfma(ax, cat(l0v, l1v), acc[tb]);
+        }
       }
     }
 
     // ---- output: acc[tb][c] = Y[t = t0 + 16 tb + l16][p = 16 wave + 4 g4 + c]
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const int t = t0 + 16 * tb + l16;
+      const int tl = 16 * tb + l16;
+      const int t = t0 + tl;
+      const u2 xw2 = DSKIP ? lds8(at(Xc, soff<8>(tl, 2 * wave + (g4 >> 1)) + (g4 & 1) * 8)) : u2{0u, 0u};
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t xw = xo[tb][c >> 1], zw = zo[tb][c >> 1];
+        const uint32_t xw = xw2[c >> 1], zw = zo[tb][c >> 1];
         const float xv = (c & 1) ? bf_hi(xw) : bf_lo(xw);
         const float zv = (c & 1) ? bf_hi(zw) : bf_lo(zw);
         float yv = acc[tb][c];
