@@ -44,22 +44,17 @@ constexpr int kP = 64;         // head width (columns per head)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kTiles = 10;     // lower-triangular 16x16 tiles of a 64x64 chunk
 
-// LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), double-buffered, stored
-// with the 16-byte units of each row permuted (unit u of row r sits at u ^ f(r)) so that both the row-wise operand
-// reads (16 rows, one unit) and the transposing reads (4 rows, 2 units) hit distinct banks.  The global->LDS copy
-// applies the permutation by choosing, per lane, which global unit to fetch.
-template <int N>
-struct alignas(16) SsdLds {
-  uint16_t B[2][kQ * N];     // B[s][n], double-buffered
-  uint16_t X[2][kQ * kP];    // x[s][p], double-buffered
-  uint16_t C[kQ * N];        // C[t][n]: its readers are done before the second barrier of a chunk, when the next
-                             // chunk's copy is issued
-  u2 M[kTiles][2][64];       // M tiles in accumulator layout: [tile][hi, lo][lane] -> 4 bf16
-  struct alignas(16) Scal {  // per-step scalars, one private copy per wave
-    float ac[kQ];            // A log2(e) cum_s
-    float phi[kQ];           // phi_s
-    float w[kQ];             // phi_s exp(A (cum_63 - cum_s))
-  } sc[4];
+// LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), stored with the 16-byte
+// units of each row permuted (unit u of row r sits at u ^ f(r)) so that both the row-wise operand reads (16 rows, one
+// unit) and the transposing reads (4 rows, 2 units) hit distinct banks; the global->LDS copy applies the permutation
+// by choosing, per lane, which global unit to fetch.  B and x are double-buffered, C (whose readers finish before the
+// second barrier of a chunk) is not.  Every buffer is its own __shared__ array and the chunk loop is unrolled by two,
+// so each access names its buffer statically: the compiler can then tell that a copy in flight into one buffer does
+// not feed a read of another, and does not wait for it.
+struct alignas(16) Scal {   // per-step scalars, one private copy per wave
+  float ac[kQ];             // A log2(e) cum_s
+  float phi[kQ];            // phi_s
+  float w[kQ];              // phi_s exp(A (cum_63 - cum_s))
 };
 
 struct SsdArgs {
@@ -78,6 +73,7 @@ struct SsdArgs {
   int H, G, hpg;
   int nchunks;
   int softplus;
+  int nbh;        // batch * nheads (the grid may be larger)
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -116,19 +112,30 @@ __device__ __forceinline__ u2 tr16(const uint16_t* p) {
   return __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p)));
 }
 
-// unit permutation of a swizzled row: f maps every 4 consecutive rows to distinct values of f >> 1 and every 16 (8)
-// consecutive rows to distinct values of f
-template <int U>
+// Unit permutations (unit u of row r is stored at u ^ f(r)), one per array and its readers, chosen for the LDS of
+// gfx950 (16-byte reads are served 8 lanes at a time over 128 bytes of banks; 8-byte and transposing reads 32 lanes
+// at a time over 256 bytes).  With r = 8a + 4b + 2c + d:
+//   B (16-row reads of one unit, and transposing reads of rows {4e..4e+3, 8+4e..} x 2 units):
+//       f = 8 (a ^ b) + 4 c + 2 d + b      (f & 7 distinct over 8 consecutive rows, f >> 1 over the transposing sets)
+//   C (16-row reads only): f = r
+//   x (128-byte rows; transposing reads of rows 4e + {0..3, 8..11} and 4g + {0..3}, and 16-row 8-byte reads):
+//       f = 4 ((r >> 2) ^ (r >> 3)) + 2 c + a
+enum { kSwzB = 0, kSwzC = 1, kSwzX = 2 };
+template <int KIND>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (U >= 16)
-    return ((r & 7) << 1) | ((r >> 3) & 1);
+  const int a = (r >> 3) & 1, b = (r >> 2) & 1, c = (r >> 1) & 1, d = r & 1;
+  if constexpr (KIND == kSwzB)
+    return 8 * (a ^ b) + 4 * c + 2 * d + b;
+  else if constexpr (KIND == kSwzC)
+    return r & 15;
   else
-    return ((r & 3) << 1) | ((r >> 2) & 1);
+    return 4 * (a ^ b) + 2 * c + a;
 }
-// byte offset of 16-byte unit u of row r in a swizzled array with U units per row
-template <int U>
+// byte offset of 16-byte unit u of row r in a permuted array with U units per row (U >= 8; for U = 8 the
+// permutation is folded to 3 bits)
+template <int U, int KIND>
 __device__ __forceinline__ int soff(int r, int u) {
-  return (r * U + (u ^ swz<U>(r))) * 16;
+  return (r * U + (u ^ (swz<KIND>(r) & (U - 1)))) * 16;
 }
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -143,7 +150,7 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
 
 // Global->LDS copies of chunk ck.  Each instruction moves 1 KB: lane i fills physical unit 64 k + i of the array.
 // Rows past the sequence read as zero (buffer range check).
-template <int U>
+template <int U, int KIND>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t rsrc, int wave, int lane, int t0,
                                            int L, int row_elems, int col0) {
   constexpr int kInstr = kQ * U / 64;
@@ -151,7 +158,7 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t
   for (int i = 0; i < kInstr / 4; ++i) {
     const int k = wave + 4 * i;
     const int P = 64 * k + lane;
-    const int r = P / U, u = (P % U) ^ swz<U>(r);
+    const int r = P / U, u = (P % U) ^ (swz<KIND>(r) & (U - 1));
     const int t = t0 + r;
     const uint32_t o = t < L ? static_cast<uint32_t>((int64_t(t) * row_elems + col0 + 8 * u) * 2) : kDropOffset;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 512 * k), 16, static_cast<int>(o), 0, 0, 0);
@@ -159,6 +166,16 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_vm4() { __builtin_amdgcn_s_waitcnt(0x0F74); }   // vmcnt(4)
+// Workgroup barrier for LDS data written by ds_write only: waits for this wave's LDS operations (lgkmcnt(0)), not
+// for its global->LDS copies in flight (which __syncthreads would also wait for).  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int N, typename TY, bool ZOH, bool GATE, bool DSKIP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N <= 128 ? 2 : 1)))
@@ -166,13 +183,21 @@ ssd_fwd_kernel(SsdArgs a) {
   constexpr int U = N / 8;
   constexpr int NB = N / 16;   // 16-row state tiles per wave
   constexpr int NK = N / 32;   // 32-deep k-steps over the state
-  __shared__ SsdLds<N> S;
+  __shared__ alignas(16) uint16_t sB0[kQ * N], sB1[kQ * N];    // B[s][n], double-buffered
+  __shared__ alignas(16) uint16_t sX0[kQ * kP], sX1[kQ * kP];  // x[s][p], double-buffered
+  __shared__ alignas(16) uint16_t sC[kQ * N];                  // C[t][n]
+  __shared__ u2 sM[kTiles][2][64];   // M tiles in accumulator layout: [tile][hi, lo][lane] -> 4 bf16
+  __shared__ Scal sSc[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int bh = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin by id; give each XCD a contiguous range of (batch, head) pairs so
+  // that the heads sharing a batch's B and C sit on the same L2.  The grid is rounded up to a multiple of 8.
+  const int per = static_cast<int>(gridDim.x) / 8;
+  const int bh = (static_cast<int>(blockIdx.x) % 8) * per + static_cast<int>(blockIdx.x) / 8;
+  if (bh >= a.nbh) return;
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / a.hpg;
   const int L = static_cast<int>(a.L);   // < 2^31: checked on the host
@@ -197,7 +222,7 @@ ssd_fwd_kernel(SsdArgs a) {
 
   // state tiles: hT[nb][c] = S[p = pcol][n = 16 nb + 4 g4 + c]
   // (no h0: a zero-length buffer, whose reads return 0)
-  const int64_t hcount = int64_t(gridDim.x) * kP * N;
+  const int64_t hcount = int64_t(a.nbh) * kP * N;
   const auto rh0 = make_rsrc(a.h0 ? a.h0 : a.A, a.h0 ? hcount : 0);
   f4 hT[NB];
 #pragma unroll
@@ -213,19 +238,24 @@ ssd_fwd_kernel(SsdArgs a) {
   };
   const int grow = a.G * N, gcol = g * N;          // B / C: row stride and column offset of this group
   const int xrow_e = a.H * kP, xcol = h * kP;      // x: row stride and column offset of this head
-  stage_rows<U>(S.B[0], rB, wave, lane, 0, L, grow, gcol);
-  stage_rows<U>(S.C, rC, wave, lane, 0, L, grow, gcol);
-  stage_rows<8>(S.X[0], rx, wave, lane, 0, L, xrow_e, xcol);
+  stage_rows<U, kSwzB>(sB0, rB, wave, lane, 0, L, grow, gcol);
+  stage_rows<U, kSwzC>(sC, rC, wave, lane, 0, L, grow, gcol);
+  stage_rows<8, kSwzX>(sX0, rx, wave, lane, 0, L, xrow_e, xcol);
   uint32_t dtw = load_dt(0);
-  auto& sc = S.sc[wave];
+  Scal& sc = sSc[wave];
 
-  for (int ck = 0; ck < a.nchunks; ++ck) {
+  // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
+  auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn)
+      __attribute__((always_inline)) {
     const int t0 = ck * kQ;
-    const int cb = ck & 1;
-    const uint16_t* Bc = S.B[cb];
-    const uint16_t* Cc = S.C;
-    const uint16_t* Xc = S.X[cb];
-    wait_vm0();                             // this wave's copies of chunk ck (and its dt) have landed
+    const uint16_t* Cc = sC;
+    // This wave's copies of chunk ck and its dt have landed.  The memory counter completes in issue order, and the
+    // last 4 operations of a chunk are the 4 output stores (one per 16-step block, always issued): after the first
+    // chunk those may stay in flight.
+    if (ck == 0)
+      wait_vm0();
+    else
+      wait_vm4();
     {
       // per-step scalars (every wave computes its own copy): Delta, phi, running sum, decay weights
       const float u = bf_lo(dtw) + bias;
@@ -244,11 +274,7 @@ ssd_fwd_kernel(SsdArgs a) {
       sc.w[lane] = ph * hw_exp2(ac63 - acv);
     }
     __syncthreads();                        // chunk ck is in LDS everywhere; chunk ck-1 is finished by every wave
-    if (ck + 1 < a.nchunks) {
-      stage_rows<U>(S.B[cb ^ 1], rB, wave, lane, t0 + kQ, L, grow, gcol);
-      stage_rows<8>(S.X[cb ^ 1], rx, wave, lane, t0 + kQ, L, xrow_e, xcol);
-      dtw = load_dt(ck + 1);
-    }
+    // (issued before the next chunk's copies: the wait for z then leaves those in flight)
     // z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
     u2 zo[4];
 #pragma unroll
@@ -259,6 +285,10 @@ ssd_fwd_kernel(SsdArgs a) {
       zo[tb] = GATE ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<int>(o), 0, 0))
                     : u2{0u, 0u};
     }
+    // the next chunk's copies (past the last chunk they read zeros into a buffer nobody reads)
+    stage_rows<U, kSwzB>(Bn, rB, wave, lane, t0 + kQ, L, grow, gcol);
+    stage_rows<8, kSwzX>(Xn, rx, wave, lane, t0 + kQ, L, xrow_e, xcol);
+    dtw = load_dt(ck + 1);
     const float* sac = sc.ac;
 
     // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb
@@ -268,8 +298,8 @@ ssd_fwd_kernel(SsdArgs a) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const u4 aB = lds16(at(Bc, soff<U>(16 * sb + l16, 4 * kk + g4)));
-        const u4 bC = lds16(at(Cc, soff<U>(16 * tb + l16, 4 * kk + g4)));
+        const u4 aB = lds16(at(Bc, soff<U, kSwzB>(16 * sb + l16, 4 * kk + g4)));
+        const u4 bC = lds16(at(Cc, soff<U, kSwzC>(16 * tb + l16, 4 * kk + g4)));
         acc = mfma(aB, bC, acc);
       }
       // acc[c] = CB[t = 16 tb + l16][s = 16 sb + 4 g4 + c]
@@ -285,8 +315,8 @@ ssd_fwd_kernel(SsdArgs a) {
       }
       u2 hi, lo;
       split4(m[0], m[1], m[2], m[3], hi, lo);
-      S.M[ti][0][lane] = hi;
-      S.M[ti][1][lane] = lo;
+      sM[ti][0][lane] = hi;
+      sM[ti][1][lane] = lo;
     }
 
     // ---- inter-chunk part: Y^T[p][t] = sum_n S_prev[p][n] C[t][n], scaled by E_t = exp2(ac_t)
@@ -304,8 +334,8 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int t = 16 * tb + l16;
-        const u2 c0 = lds8(at(Cc, soff<U>(t, 4 * kn + (g4 >> 1)) + half));
-        const u2 c1 = lds8(at(Cc, soff<U>(t, 4 * kn + 2 + (g4 >> 1)) + half));
+        const u2 c0 = lds8(at(Cc, soff<U, kSwzC>(t, 4 * kn + (g4 >> 1)) + half));
+        const u2 c1 = lds8(at(Cc, soff<U, kSwzC>(t, 4 * kn + 2 + (g4 >> 1)) + half));
         const u4 bC = cat(c0, c1);
         acc[tb] = mfma(hh, bC, acc[tb]);
         acc[tb] = mfma(hl, bC, acc[tb]);
@@ -325,7 +355,7 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int k0 = 32 * ks + 8 * g4 + 4 * e;
-          const u2 xv = tr16(at(Xc, soff<8>(k0 + trow, (16 * wave + tcol) >> 3) + xhalf));
+          const u2 xv = tr16(at(Xc, soff<8, kSwzX>(k0 + trow, (16 * wave + tcol) >> 3) + xhalf));
           const f4 wv = *reinterpret_cast<const f4*>(&sc.w[k0]);
           split4(bf_lo(xv[0]) * wv[0], bf_hi(xv[0]) * wv[1], bf_lo(xv[1]) * wv[2], bf_hi(xv[1]) * wv[3], hp[e],
                  lp[e]);
@@ -340,8 +370,8 @@ ssd_fwd_kernel(SsdArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
           const int k0 = 32 * ks + 8 * g4;
           const int unit = (16 * nb + tcol) >> 3;
-          const u2 b0 = tr16(at(Bc, soff<U>(k0 + trow, unit) + xhalf));
-          const u2 b1 = tr16(at(Bc, soff<U>(k0 + 4 + trow, unit) + xhalf));
+          const u2 b0 = tr16(at(Bc, soff<U, kSwzB>(k0 + trow, unit) + xhalf));
+          const u2 b1 = tr16(at(Bc, soff<U, kSwzB>(k0 + 4 + trow, unit) + xhalf));
           const u4 aB = cat(b0, b1);
           st = mfma(aB, xh[ks], st);
           st = mfma(aB, xl[ks], st);
@@ -349,8 +379,8 @@ ssd_fwd_kernel(SsdArgs a) {
         hT[nb] = st;
       }
     }
-    __syncthreads();                        // M tiles are in LDS; every wave is done with C
-    if (ck + 1 < a.nchunks) stage_rows<U>(S.C, rC, wave, lane, t0 + kQ, L, grow, gcol);
+    lds_barrier();                          // M tiles are in LDS; every wave is done with C
+    stage_rows<U, kSwzC>(sC, rC, wave, lane, t0 + kQ, L, grow, gcol);
 
     // ---- intra-chunk part: Y^T[p][t] += sum_{s <= t} x^T[p][s] M[t][s]
     {
@@ -359,8 +389,8 @@ ssd_fwd_kernel(SsdArgs a) {
       for (int kk = 0; kk < 2; ++kk) {
         // k-set: s = 32 kk + 4 g4 + c (tile sb = 2kk) and 32 kk + 16 + 4 g4 + c (tile 2kk+1)
         const int unit = (16 * wave + tcol) >> 3;
-        const u2 x0 = tr16(at(Xc, soff<8>(32 * kk + 4 * g4 + trow, unit) + xhalf));
-        const u2 x1 = tr16(at(Xc, soff<8>(32 * kk + 16 + 4 * g4 + trow, unit) + xhalf));
+        const u2 x0 = tr16(at(Xc, soff<8, kSwzX>(32 * kk + 4 * g4 + trow, unit) + xhalf));
+        const u2 x1 = tr16(at(Xc, soff<8, kSwzX>(32 * kk + 16 + 4 * g4 + trow, unit) + xhalf));
         const u4 ax = cat(x0, x1);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -368,10 +398,10 @@ ssd_fwd_kernel(SsdArgs a) {
           const int sb0 = 2 * kk, sb1 = 2 * kk + 1;
           const int t0i = tb * (tb + 1) / 2;
           const u2 zero = {0u, 0u};
-          const u2 h0v = S.M[t0i + sb0][0][lane];
-          const u2 l0v = S.M[t0i + sb0][1][lane];
-          const u2 h1v = sb1 <= tb ? S.M[t0i + sb1][0][lane] : zero;
-          const u2 l1v = sb1 <= tb ? S.M[t0i + sb1][1][lane] : zero;
+          const u2 h0v = sM[t0i + sb0][0][lane];
+          const u2 l0v = sM[t0i + sb0][1][lane];
+          const u2 h1v = sb1 <= tb ? sM[t0i + sb1][0][lane] : zero;
+          const u2 l1v = sb1 <= tb ? sM[t0i + sb1][1][lane] : zero;
           acc[tb] = mfma(ax, cat(h0v, h1v), acc[tb]);
           acc[tb] = mfma(ax, cat(l0v, l1v), acc[tb]);
         }
@@ -383,7 +413,7 @@ ssd_fwd_kernel(SsdArgs a) {
     for (int tb = 0; tb < 4; ++tb) {
       const int tl = 16 * tb + l16;
       const int t = t0 + tl;
-      const u2 xw2 = DSKIP ? lds8(at(Xc, soff<8>(tl, 2 * wave + (g4 >> 1)) + (g4 & 1) * 8)) : u2{0u, 0u};
+      const u2 xw2 = DSKIP ? lds8(at(Xc, soff<8, kSwzX>(tl, 2 * wave + (g4 >> 1)) + (g4 & 1) * 8)) : u2{0u, 0u};
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -406,6 +436,10 @@ ssd_fwd_kernel(SsdArgs a) {
         __builtin_amdgcn_raw_buffer_store_b64(ov, ry, static_cast<int>(o), 0, 0);
       }
     }
+    };
+  for (int ck = 0; ck < a.nchunks; ck += 2) {
+    chunk(ck, sB0, sX0, sB1, sX1);
+    if (ck + 1 < a.nchunks) chunk(ck + 1, sB1, sX1, sB0, sX0);
   }
 
   if (a.h_final) {
@@ -579,7 +613,8 @@ extern "C" ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const 
   a.hpg = static_cast<int>(p->nheads / p->ngroups);
   a.nchunks = static_cast<int>((p->seqlen + kQ - 1) / kQ);
   a.softplus = p->dt_softplus;
-  const int grid = static_cast<int>(p->batch * p->nheads);
+  a.nbh = static_cast<int>(p->batch * p->nheads);
+  const int grid = (a.nbh + 7) / 8 * 8;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool gate = z != nullptr, dskip = Dskip != nullptr;
   switch (p->dstate) {
