@@ -316,9 +316,12 @@ def main():
         ys = torch.empty((sb, sL, sH, sP), dtype=torch.bfloat16, device=dev)
         hfs = torch.empty((sb, sH, sP, sN), dtype=torch.float32, device=dev)
         spar = _abi.make_ssd_params(sb, sL, sH, sP, sG, sN, ssm.SSM_BF16, ssm.SSM_BF16)
+        snseg = _abi.ssd_plan_segments(spar)
+        sws_n = _abi.ssd_workspace_bytes(spar)
+        sws = torch.empty(max(sws_n, 1), dtype=torch.uint8, device=dev)
         sargs = (sd["x"].data_ptr(), sd["dt"].data_ptr(), sd["dt_bias"].data_ptr(), sd["A"].data_ptr(),
                  sd["B"].data_ptr(), sd["C"].data_ptr(), sd["Dskip"].data_ptr(), sd["z"].data_ptr(), 0,
-                 ys.data_ptr(), hfs.data_ptr(), stream.cuda_stream)
+                 ys.data_ptr(), hfs.data_ptr(), sws.data_ptr() if sws_n else 0, sws_n, stream.cuda_stream)
 
         def sstep():
             st = _abi.ssd_fwd_raw(spar, *sargs)
@@ -341,7 +344,7 @@ def main():
         stf = sfl / (sms * 1e-3) / 1e12
         selem = sb * sL * sH * sP
         out["ssd"] = {"workload": "mamba2-2.7b-layer: batch %d, seqlen %d, %d heads x %d, ngroups %d, d_state %d, "
-                                  "bf16 io, gate + D" % (sb, sL, sH, sP, sG, sN),
+                                  "bf16 io, gate + D, %d L-segments" % (sb, sL, sH, sP, sG, sN, snseg),
                       "ms_per_step": sms, "elements_per_s": selem / (sms * 1e-3),
                       "ratio_to_s6_scan_same_elements": sms / ms if selem == elems else None,
                       "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

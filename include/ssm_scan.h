@@ -212,8 +212,15 @@ typedef struct {
   int32_t y_dtype;     /* SSM_BF16 or SSM_F32 */
   int32_t disc;        /* ssm_disc */
   int32_t dt_softplus; /* 1: Delta = softplus(dt + dt_bias); 0: Delta = dt + dt_bias */
-  int32_t reserved;    /* must be 0 */
+  int32_t segments;    /* 0: the library picks how many L-segments run in parallel; k > 0 forces k (clamped to the
+                          number of 64-step chunks); results agree within rounding either way */
 } ssm_ssd_params;
+
+/* Bytes of device workspace ssm_ssd_fwd needs (0 when it runs as one segment).  Pure host function. */
+size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_params* p);
+
+/* Number of L-segments ssm_ssd_fwd uses for these parameters (>= 1), or 0 for invalid parameters. */
+int ssm_ssd_fwd_plan_segments(const ssm_ssd_params* p);
 
 /*
  * SSD forward over full sequences.  Layouts (row-major, heads inside time, as the pages' (batch, length, channels)):
@@ -221,12 +228,15 @@ typedef struct {
  *   B, C [batch][seqlen][ngroups][dstate] bf16;  A, dt_bias, Dskip [nheads] fp32 (dt_bias / Dskip NULL = 0 / none);
  *   h0, h_final [batch][nheads][headdim][dstate] fp32 or NULL (h0 NULL = zeros; h_final may alias h0);
  *   y [batch][seqlen][nheads][headdim] y_dtype.
- * x, B, C, z, y, h0 and h_final must be 16-byte aligned.  No workspace.  Errors as for ssm_scan_fwd, plus
- * SSM_ERR_DTYPE for io_dtype != SSM_BF16 and SSM_ERR_UNSUPPORTED for headdim != 64 or dstate not in {64, 128, 256}.
+ * x, B, C, z, y, h0 and h_final must be 16-byte aligned.  workspace: device buffer of at least
+ * ssm_ssd_fwd_workspace_bytes(p) bytes, 16-byte aligned (NULL if 0 are needed): with more than one segment a first
+ * pass writes each segment's end state from a zero start there, and every segment starts from h0 carried through the
+ * segments before it.  Errors as for ssm_scan_fwd, plus SSM_ERR_DTYPE for io_dtype != SSM_BF16 and
+ * SSM_ERR_UNSUPPORTED for headdim != 64, dstate not in {64, 128, 256} or negative segments.
  */
 ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
                        const void* B, const void* C, const float* Dskip, const void* z, const float* h0, void* y,
-                       float* h_final, void* stream);
+                       float* h_final, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One SSD decode step: state [batch][nheads][headdim][dstate] fp32 (16-byte aligned) updated in place;
  * x, z, y [batch][nheads][headdim];  dt [batch][nheads];  B, C [batch][ngroups][dstate] (8-byte aligned). */

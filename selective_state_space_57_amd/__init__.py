@@ -14,7 +14,7 @@ from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_param
                    bwd_workspace_bytes)
 
 __all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "complex_scan_fwd",
-           "complex_state_update", "ssd_fwd", "ssd_state_update", "EULER_B", "ZOH", "SSMError",
+           "complex_state_update", "ssd_fwd", "ssd_state_update", "ssd_workspace_bytes", "EULER_B", "ZOH", "SSMError",
            "Params", "make_params", "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
@@ -317,9 +317,11 @@ def state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=N
 
 
 def ssd_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=None, h_final=None, y_dtype=None,
-            disc=EULER_B, softplus=True, return_final_state=True, stream=None):
+            disc=EULER_B, softplus=True, segments=0, workspace=None, return_final_state=True, stream=None):
     """Mamba-2 SSD layer.  x, z (b, L, H, P) bfloat16; dt (b, L, H) bfloat16; B, C (b, L, G, N) bfloat16; A, dt_bias,
-    Dskip (H,) float32; h0 / h_final (b, H, P, N) float32.  Returns (y (b, L, H, P), h_final)."""
+    Dskip (H,) float32; h0 / h_final (b, H, P, N) float32.  segments: 0 = the library's choice of L-segments.
+    workspace: a uint8 device tensor of at least ssd_workspace_bytes(...) bytes (allocated here when None).
+    Returns (y (b, L, H, P), h_final)."""
     import torch
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -334,15 +336,25 @@ def ssd_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=None
                                    ("h0", h0, (b, H, P, N), f32, True), ("y", y, (b, L, H, P), ydt, True),
                                    ("h_final", h_final, (b, H, P, N), f32, True)):
         _expect(name, t, shp, dtp, dev, optional=opt)
-    p = _abi.make_ssd_params(b, L, H, P, G, N, io, io_code(ydt), disc, softplus)
+    p = _abi.make_ssd_params(b, L, H, P, G, N, io, io_code(ydt), disc, softplus, segments)
     if y is None:
         y = torch.empty((b, L, H, P), dtype=ydt, device=dev)
     if h_final is None and return_final_state:
         h_final = torch.empty((b, H, P, N), dtype=f32, device=dev)
+    ws_need = _abi.ssd_workspace_bytes(p)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _abi.ssd_fwd_raw(p, _addr(x), _addr(dt), _addr(dt_bias), _addr(A), _addr(B), _addr(C), _addr(Dskip),
-                          _addr(z), _addr(h0), _addr(y), _addr(h_final), _stream_handle(stream, dev))
+                          _addr(z), _addr(h0), _addr(y), _addr(h_final), _addr(workspace), ws_bytes,
+                          _stream_handle(stream, dev))
     _abi.check(st)
     return y, h_final
+
+
+def ssd_workspace_bytes(b, L, H, P, G, N, segments=0) -> int:
+    """Workspace bytes ssd_fwd needs for these sizes (bf16 io)."""
+    return _abi.ssd_workspace_bytes(_abi.make_ssd_params(b, L, H, P, G, N, SSM_BF16, SSM_BF16, segments=segments))
 
 
 def ssd_state_update(state, x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, *, y=None, y_dtype=None, disc=EULER_B,

@@ -18,7 +18,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE"
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
            "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update",
-           "ssm_ssd_fwd", "ssm_ssd_state_update"]
+           "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan_segments"]
 
 
 class Params(ctypes.Structure):
@@ -37,7 +37,7 @@ class SsdParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
-                ("dt_softplus", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dt_softplus", ctypes.c_int32), ("segments", ctypes.c_int32)]
 
 
 class SSMError(RuntimeError):
@@ -82,8 +82,12 @@ def lib():
         L.ssm_complex_state_update.argtypes = [PP] + [P] * 11
         L.ssm_complex_state_update.restype = ctypes.c_int
         SP = ctypes.POINTER(SsdParams)
-        L.ssm_ssd_fwd.argtypes = [SP] + [P] * 12
+        L.ssm_ssd_fwd.argtypes = [SP] + [P] * 11 + [P, S, P]
         L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_ssd_fwd_workspace_bytes.argtypes = [SP]
+        L.ssm_ssd_fwd_workspace_bytes.restype = S
+        L.ssm_ssd_fwd_plan_segments.argtypes = [SP]
+        L.ssm_ssd_fwd_plan_segments.restype = ctypes.c_int
         L.ssm_ssd_state_update.argtypes = [SP] + [P] * 11
         L.ssm_ssd_state_update.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
@@ -102,13 +106,22 @@ def make_params(batch, dim, seqlen, dstate, io_dtype=SSM_BF16, y_dtype=None, dis
 
 
 def make_ssd_params(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype=SSM_BF16, y_dtype=None, disc=EULER_B,
-                    softplus=True) -> SsdParams:
+                    softplus=True, segments=0) -> SsdParams:
     return SsdParams(int(batch), int(seqlen), int(nheads), int(headdim), int(ngroups), int(dstate), int(io_dtype),
-                     int(io_dtype if y_dtype is None else y_dtype), int(disc), int(bool(softplus)), 0)
+                     int(io_dtype if y_dtype is None else y_dtype), int(disc), int(bool(softplus)), int(segments))
 
 
-def ssd_fwd_raw(p: SsdParams, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream):
-    return lib().ssm_ssd_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream)
+def ssd_workspace_bytes(p: SsdParams) -> int:
+    return int(lib().ssm_ssd_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def ssd_plan_segments(p: SsdParams) -> int:
+    return int(lib().ssm_ssd_fwd_plan_segments(ctypes.byref(p)))
+
+
+def ssd_fwd_raw(p: SsdParams, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace, workspace_bytes_, stream):
+    return lib().ssm_ssd_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
+                             workspace_bytes_, stream)
 
 
 def ssd_state_update_raw(p: SsdParams, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):

@@ -73,7 +73,11 @@ struct SsdArgs {
   int H, G, hpg;
   int nchunks;
   int softplus;
-  int nbh;        // batch * nheads (the grid may be larger)
+  int nbh;        // batch * nheads
+  int nseg, cps;  // L-segments and chunks per segment
+  int nwork;      // work items of this launch (the grid may be larger)
+  float* ws_state;  // [b][h][nseg-1][P][N]: end state of each segment but the last, from a zero start
+  float* ws_sum;    // [b][h][nseg-1]: sum of Delta over each segment but the last
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -138,18 +142,25 @@ __device__ __forceinline__ int soff(int r, int u) {
   return (r * U + (u ^ (swz<KIND>(r) & (U - 1)))) * 16;
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave: within each 16-lane row by DPP row shifts (a lane whose source
+// lies before its row reads 0), then the totals of the rows before it, read from lanes 15, 31 and 47
+template <int K>
+__device__ __forceinline__ float row_shr(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + K, 0xf, 0xf,
+                                                               false));
+}
 __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float o = __shfl_up(v, d, 64);
-    v += lane >= d ? o : 0.0f;
-  }
-  return v;
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f) + (row >= 3 ? r2 : 0.0f);
 }
 
-// Global->LDS copies of chunk ck.  Each instruction moves 1 KB: lane i fills physical unit 64 k + i of the array.
-// Rows past the sequence read as zero (buffer range check).
 template <int U, int KIND>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t rsrc, int wave, int lane, int t0,
                                            int L, int row_elems, int col0) {
@@ -177,7 +188,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int N, typename TY, bool ZOH, bool GATE, bool DSKIP>
+// SEGST: the first pass over a segment (every segment but the last) that only runs the state recurrence from a zero
+// state and writes the segment's end state and its sum of Delta.  Otherwise the full layer over one segment, starting
+// from h0 carried through the segments before it.
+template <int N, typename TY, bool ZOH, bool GATE, bool DSKIP, bool SEGST>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N <= 128 ? 2 : 1)))
 ssd_fwd_kernel(SsdArgs a) {
   constexpr int U = N / 8;
@@ -193,12 +207,19 @@ ssd_fwd_kernel(SsdArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Workgroups are dealt to the 8 XCDs round-robin by id; give each XCD a contiguous range of (batch, head) pairs so
-  // that the heads sharing a batch's B and C sit on the same L2.  The grid is rounded up to a multiple of 8.
+  // Workgroups are dealt to the 8 XCDs round-robin by id; give each XCD a contiguous range of work items, ordered
+  // (batch, segment, head) with the head fastest, so that the heads sharing a batch's B and C sit on the same L2.
+  // The grid is rounded up to a multiple of 8.
   const int per = static_cast<int>(gridDim.x) / 8;
-  const int bh = (static_cast<int>(blockIdx.x) % 8) * per + static_cast<int>(blockIdx.x) / 8;
-  if (bh >= a.nbh) return;
-  const int b = bh / a.H, h = bh % a.H;
+  const int item = (static_cast<int>(blockIdx.x) % 8) * per + static_cast<int>(blockIdx.x) / 8;
+  if (item >= a.nwork) return;
+  const int nsegw = SEGST ? a.nseg - 1 : a.nseg;   // segments this launch covers
+  const int h = item % a.H;
+  const int seg = (item / a.H) % nsegw;
+  const int b = item / (a.H * nsegw);
+  const int bh = b * a.H + h;
+  const int c0 = seg * a.cps;
+  const int c1 = min(c0 + a.cps, a.nchunks);
   const int g = h / a.hpg;
   const int L = static_cast<int>(a.L);   // < 2^31: checked on the host
 
@@ -221,14 +242,25 @@ ssd_fwd_kernel(SsdArgs a) {
   const int trow = l16 >> 2, tcol = 4 * (l16 & 3);
 
   // state tiles: hT[nb][c] = S[p = pcol][n = 16 nb + 4 g4 + c]
-  // (no h0: a zero-length buffer, whose reads return 0)
+  // (no h0, or the zero-start pass: a zero-length buffer, whose reads return 0)
   const int64_t hcount = int64_t(a.nbh) * kP * N;
-  const auto rh0 = make_rsrc(a.h0 ? a.h0 : a.A, a.h0 ? hcount : 0);
+  const auto rh0 = make_rsrc(a.h0 && !SEGST ? a.h0 : a.A, a.h0 && !SEGST ? hcount : 0);
   f4 hT[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     hT[nb] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
                                         rh0, static_cast<int>((srow * N + 16 * nb + 4 * g4) * 4), 0, 0));
+  if constexpr (!SEGST) {
+    // carry h0 through the segments before this one: S <- exp(A sum_j Delta) S + (end state of segment j from 0)
+    for (int j = 0; j < seg; ++j) {
+      const int64_t slot = int64_t(bh) * (a.nseg - 1) + j;
+      const float dj = hw_exp2(A2 * a.ws_sum[slot]);
+      const float* st = a.ws_state + (slot * kP + pcol) * N + 4 * g4;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) hT[nb] = hT[nb] * dj + *reinterpret_cast<const f4*>(st + 16 * nb);
+    }
+  }
+  float dsum = 0.0f;   // sum of Delta over this segment (zero-start pass)
 
   auto load_dt = [&](int ck) -> uint32_t {
     const int t = ck * kQ + lane;
@@ -238,10 +270,10 @@ ssd_fwd_kernel(SsdArgs a) {
   };
   const int grow = a.G * N, gcol = g * N;          // B / C: row stride and column offset of this group
   const int xrow_e = a.H * kP, xcol = h * kP;      // x: row stride and column offset of this head
-  stage_rows<U, kSwzB>(sB0, rB, wave, lane, 0, L, grow, gcol);
-  stage_rows<U, kSwzC>(sC, rC, wave, lane, 0, L, grow, gcol);
-  stage_rows<8, kSwzX>(sX0, rx, wave, lane, 0, L, xrow_e, xcol);
-  uint32_t dtw = load_dt(0);
+  stage_rows<U, kSwzB>(sB0, rB, wave, lane, c0 * kQ, L, grow, gcol);
+  if constexpr (!SEGST) stage_rows<U, kSwzC>(sC, rC, wave, lane, c0 * kQ, L, grow, gcol);
+  stage_rows<8, kSwzX>(sX0, rx, wave, lane, c0 * kQ, L, xrow_e, xcol);
+  uint32_t dtw = load_dt(c0);
   Scal& sc = sSc[wave];
 
   // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
@@ -251,8 +283,8 @@ ssd_fwd_kernel(SsdArgs a) {
     const uint16_t* Cc = sC;
     // This wave's copies of chunk ck and its dt have landed.  The memory counter completes in issue order, and the
     // last 4 operations of a chunk are the 4 output stores (one per 16-step block, always issued): after the first
-    // chunk those may stay in flight.
-    if (ck == 0)
+    // chunk of the full pass those may stay in flight.
+    if (SEGST || ck == c0)
       wait_vm0();
     else
       wait_vm4();
@@ -268,7 +300,8 @@ ssd_fwd_kernel(SsdArgs a) {
       }
       const float cum = wave_incl_scan(dl, lane);
       const float acv = cum * A2;
-      const float ac63 = __shfl(acv, 63, 64);
+      const float ac63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acv), 63));
+      if constexpr (SEGST) dsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
       sc.ac[lane] = acv;
       sc.phi[lane] = ph;
       sc.w[lane] = ph * hw_exp2(ac63 - acv);
@@ -279,6 +312,10 @@ ssd_fwd_kernel(SsdArgs a) {
     u2 zo[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      if constexpr (SEGST) {
+        zo[tb] = u2{0u, 0u};
+        continue;
+      }
       const int t = t0 + 16 * tb + l16;
       const uint32_t o = t < L ? static_cast<uint32_t>(((int64_t(t) * a.H + h) * kP + 16 * wave + 4 * g4) * 2)
                                : kDropOffset;
@@ -292,7 +329,7 @@ ssd_fwd_kernel(SsdArgs a) {
     const float* sac = sc.ac;
 
     // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb
-    for (int ti = wave; ti < kTiles; ti += 4) {
+    for (int ti = wave; ti < (SEGST ? 0 : kTiles); ti += 4) {
       const int tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
       const int sb = ti - tb * (tb + 1) / 2;
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -324,7 +361,7 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[tb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kn = 0; kn < NK; ++kn) {
+    for (int kn = 0; kn < (SEGST ? 0 : NK); ++kn) {
       // k-set of this lane: n = 32 kn + 4 g4 + c (tile 2kn) and 32 kn + 16 + 4 g4 + c (tile 2kn+1)
       u2 h0h, h0l, h1h, h1l;
       split4(hT[2 * kn][0], hT[2 * kn][1], hT[2 * kn][2], hT[2 * kn][3], h0h, h0l);
@@ -341,8 +378,10 @@ ssd_fwd_kernel(SsdArgs a) {
         acc[tb] = mfma(hl, bC, acc[tb]);
       }
     }
+    if constexpr (!SEGST) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) acc[tb] *= hw_exp2(sac[16 * tb + l16]);
+      for (int tb = 0; tb < 4; ++tb) acc[tb] *= hw_exp2(sac[16 * tb + l16]);
+    }
 
     // ---- state update: S_next^T[n][p] = exp2(ac_63) S_prev^T[n][p] + sum_s B^T[n][s] (w_s x[s][p])
     {
@@ -379,6 +418,7 @@ ssd_fwd_kernel(SsdArgs a) {
         hT[nb] = st;
       }
     }
+    if constexpr (SEGST) return;            // the zero-start pass only carries the state
     lds_barrier();                          // M tiles are in LDS; every wave is done with C
     stage_rows<U, kSwzC>(sC, rC, wave, lane, t0 + kQ, L, grow, gcol);
 
@@ -437,12 +477,18 @@ ssd_fwd_kernel(SsdArgs a) {
       }
     }
     };
-  for (int ck = 0; ck < a.nchunks; ck += 2) {
+  for (int ck = c0; ck < c1; ck += 2) {
     chunk(ck, sB0, sX0, sB1, sX1);
-    if (ck + 1 < a.nchunks) chunk(ck + 1, sB1, sX1, sB0, sX0);
+    if (ck + 1 < c1) chunk(ck + 1, sB1, sX1, sB0, sX0);
   }
 
-  if (a.h_final) {
+  if constexpr (SEGST) {
+    const int64_t slot = int64_t(bh) * (a.nseg - 1) + seg;
+    float* st = a.ws_state + (slot * kP + pcol) * N + 4 * g4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(st + 16 * nb) = hT[nb];
+    if (tid == 0) a.ws_sum[slot] = dsum;
+  } else if (a.h_final && seg == a.nseg - 1) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(a.h_final + srow * N + 16 * nb + 4 * g4) = hT[nb];
   }
@@ -529,7 +575,7 @@ ssm_status check_ssd(const ssm_ssd_params* p, bool need_seqlen) {
   if (p->disc != SSM_DISC_EULER_B && p->disc != SSM_DISC_ZOH) return fail(SSM_ERR_UNSUPPORTED, "unknown disc %d", p->disc);
   if (p->dt_softplus != 0 && p->dt_softplus != 1)
     return fail(SSM_ERR_UNSUPPORTED, "dt_softplus must be 0 or 1 (got %d)", p->dt_softplus);
-  if (p->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved must be 0");
+  if (p->segments < 0) return fail(SSM_ERR_UNSUPPORTED, "segments must be >= 0 (got %d)", p->segments);
   const int64_t L = need_seqlen ? p->seqlen : 1;
   // buffer offsets are 32-bit: one batch element of x / y (fp32 y: 4 bytes) and of B / C must stay below 2^31 bytes
   if (L * p->nheads * kP * 4 >= (int64_t(1) << 31) || L * p->ngroups * p->dstate * 2 >= (int64_t(1) << 31))
@@ -538,27 +584,61 @@ ssm_status check_ssd(const ssm_ssd_params* p, bool need_seqlen) {
   return SSM_OK;
 }
 
-template <int N, typename TY, bool ZOH>
-ssm_status launch_fwd(const SsdArgs& a, int grid, bool gate, bool dskip, hipStream_t st) {
-  if (gate && dskip)
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, true, true>), dim3(grid), dim3(kThreads), 0, st, a);
+template <int N, typename TY, bool ZOH, bool SEGST>
+ssm_status launch_fwd(const SsdArgs& a, bool gate, bool dskip, hipStream_t st) {
+  const int grid = (a.nwork + 7) / 8 * 8;
+  if (SEGST)   // the zero-start pass never touches y, z or Dskip
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, false, false, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else if (gate && dskip)
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, true, true, false>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (gate)
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, true, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, true, false, false>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (dskip)
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, false, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, false, true, false>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, false, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, TY, ZOH, false, false, false>), dim3(grid), dim3(kThreads), 0, st, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SSM_OK : fail(SSM_ERR_HIP, "ssd_fwd_kernel launch: %s", hipGetErrorString(e));
 }
 
+// with more than one segment: the zero-start pass over every segment but the last, then the full pass
 template <int N>
-ssm_status dispatch_fwd(const ssm_ssd_params* p, const SsdArgs& a, int grid, bool gate, bool dskip, hipStream_t st) {
+ssm_status dispatch_fwd(const ssm_ssd_params* p, SsdArgs a, bool gate, bool dskip, hipStream_t st) {
   const bool zoh = p->disc == SSM_DISC_ZOH;
+  if (a.nseg > 1) {
+    SsdArgs s1 = a;
+    s1.nwork = a.nbh * (a.nseg - 1);
+    const ssm_status r = zoh ? launch_fwd<N, uint16_t, true, true>(s1, false, false, st)
+                             : launch_fwd<N, uint16_t, false, true>(s1, false, false, st);
+    if (r != SSM_OK) return r;
+  }
+  a.nwork = a.nbh * a.nseg;
   if (p->y_dtype == SSM_F32)
-    return zoh ? launch_fwd<N, float, true>(a, grid, gate, dskip, st) : launch_fwd<N, float, false>(a, grid, gate, dskip, st);
-  return zoh ? launch_fwd<N, uint16_t, true>(a, grid, gate, dskip, st)
-             : launch_fwd<N, uint16_t, false>(a, grid, gate, dskip, st);
+    return zoh ? launch_fwd<N, float, true, false>(a, gate, dskip, st)
+               : launch_fwd<N, float, false, false>(a, gate, dskip, st);
+  return zoh ? launch_fwd<N, uint16_t, true, false>(a, gate, dskip, st)
+             : launch_fwd<N, uint16_t, false, false>(a, gate, dskip, st);
+}
+
+// Segments along L: when the (batch, head) pairs alone leave CUs idle (fewer than 256 of them), split L so that
+// there are about 1280 work items, at least one 64-step chunk each.  With 256 pairs or more one segment is kept:
+// the zero-start pass then costs about what the better balance gains.
+struct SsdPlan {
+  int nchunks, nseg, cps;
+  size_t state_bytes, sum_bytes;
+};
+SsdPlan ssd_plan(const ssm_ssd_params* p) {
+  SsdPlan pl{};
+  pl.nchunks = static_cast<int>((p->seqlen + kQ - 1) / kQ);
+  const int64_t nbh = p->batch * p->nheads;
+  int64_t want = p->segments > 0 ? p->segments : (nbh >= 256 ? 1 : (1280 + nbh - 1) / nbh);
+  want = want < 1 ? 1 : (want > pl.nchunks ? pl.nchunks : want);
+  pl.cps = static_cast<int>((pl.nchunks + want - 1) / want);
+  pl.nseg = (pl.nchunks + pl.cps - 1) / pl.cps;
+  const int64_t slots = nbh * (pl.nseg - 1);
+  pl.state_bytes = static_cast<size_t>(slots * kP * p->dstate * 4);
+  pl.sum_bytes = static_cast<size_t>((slots * 4 + 255) / 256 * 256);
+  return pl;
 }
 
 template <int N, typename TY>
@@ -585,9 +665,21 @@ ssm_status dispatch_decode(const ssm_ssd_params* p, const SsdDecodeArgs& a, hipS
 
 using namespace ssm57;
 
+extern "C" size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_params* p) {
+  if (check_ssd(p, true) != SSM_OK) return 0;
+  const SsdPlan pl = ssd_plan(p);
+  return pl.nseg > 1 ? pl.state_bytes + pl.sum_bytes : 0;
+}
+
+extern "C" int ssm_ssd_fwd_plan_segments(const ssm_ssd_params* p) {
+  if (check_ssd(p, true) != SSM_OK) return 0;
+  return ssd_plan(p).nseg;
+}
+
 extern "C" ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const void* dt, const float* dt_bias,
                                   const float* A, const void* B, const void* C, const float* Dskip, const void* z,
-                                  const float* h0, void* y, float* h_final, void* stream) {
+                                  const float* h0, void* y, float* h_final, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   g_err[0] = 0;
   if (ssm_status s = check_ssd(p, true); s != SSM_OK) return s;
   if (!x || !dt || !A || !B || !C || !y) return fail(SSM_ERR_NULL, "x, dt, A, B, C and y are required");
@@ -595,6 +687,11 @@ extern "C" ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const 
       !aligned(dt, 2) || (h0 && !aligned(h0, 16)) || (h_final && !aligned(h_final, 16)) || !aligned(A, 4) ||
       (dt_bias && !aligned(dt_bias, 4)) || (Dskip && !aligned(Dskip, 4)))
     return fail(SSM_ERR_ALIGN, "x, B, C, z, y, h0 and h_final must be 16-byte aligned");
+  const SsdPlan pl = ssd_plan(p);
+  const size_t need = pl.nseg > 1 ? pl.state_bytes + pl.sum_bytes : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu at %p", need,
+                workspace_bytes, workspace);
   SsdArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.dt = static_cast<const uint16_t*>(dt);
@@ -611,16 +708,20 @@ extern "C" ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const 
   a.H = static_cast<int>(p->nheads);
   a.G = static_cast<int>(p->ngroups);
   a.hpg = static_cast<int>(p->nheads / p->ngroups);
-  a.nchunks = static_cast<int>((p->seqlen + kQ - 1) / kQ);
+  a.nchunks = pl.nchunks;
   a.softplus = p->dt_softplus;
   a.nbh = static_cast<int>(p->batch * p->nheads);
-  const int grid = (a.nbh + 7) / 8 * 8;
+  a.nseg = pl.nseg;
+  a.cps = pl.cps;
+  a.ws_state = pl.nseg > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_sum = pl.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.state_bytes) : nullptr;
+  if (int64_t(a.nbh) * a.nseg >= (int64_t(1) << 31) - 8) return fail(SSM_ERR_SHAPE, "too many work items");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool gate = z != nullptr, dskip = Dskip != nullptr;
   switch (p->dstate) {
-    case 64: return dispatch_fwd<64>(p, a, grid, gate, dskip, st);
-    case 128: return dispatch_fwd<128>(p, a, grid, gate, dskip, st);
-    default: return dispatch_fwd<256>(p, a, grid, gate, dskip, st);
+    case 64: return dispatch_fwd<64>(p, a, gate, dskip, st);
+    case 128: return dispatch_fwd<128>(p, a, gate, dskip, st);
+    default: return dispatch_fwd<256>(p, a, gate, dskip, st);
   }
 }
 

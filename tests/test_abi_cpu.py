@@ -166,22 +166,20 @@ def SP(**kw):
     return _abi.make_ssd_params(**base)
 
 
-def call_ssd(p, **ptrs):
+def call_ssd(p, ws=0, ws_bytes=0, **ptrs):
     names = ["x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "h0", "y", "h_final"]
     v = {k: FAKE for k in ["x", "dt", "A", "B", "C", "y"]}
     v.update(ptrs)
-    return _abi.ssd_fwd_raw(p, *[v.get(k, 0) for k in names], 0)
+    return _abi.ssd_fwd_raw(p, *[v.get(k, 0) for k in names], ws, ws_bytes, 0)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2), (dict(headdim=32), 4),
     (dict(dstate=16), 4), (dict(dstate=96), 4), (dict(io_dtype=_abi.SSM_F32), 3), (dict(y_dtype=7), 3),
-    (dict(disc=2), 4), (dict(softplus=True), 0),
+    (dict(disc=2), 4),
 ])
 def test_ssd_param_errors(lib, kw, code):
     p = SP(**kw)
-    if code == 0:
-        return                              # the valid base case is not launched on the CPU
     assert call_ssd(p) == code
     assert lib.ssm_last_error().decode()
 
@@ -192,9 +190,25 @@ def test_ssd_null_and_align(lib):
     for k in ["x", "B", "C", "y"]:
         assert call_ssd(SP(), **{k: FAKE + 8}) == 5, k
     p = SP()
-    p.reserved = 1
+    p.segments = -1
     assert call_ssd(p) == 4
     names = ["state", "x", "dt", "dt_bias", "A", "B", "C", "Dskip", "z", "y"]
     v = {k: FAKE for k in ["state", "x", "dt", "A", "B", "C", "y"]}
     assert _abi.ssd_state_update_raw(SP(dstate=32), *[v.get(k, 0) for k in names], 0) == 4
     assert _abi.ssd_state_update_raw(SP(), *[0 if k == "state" else v.get(k, 0) for k in names], 0) == 1
+
+
+def test_ssd_workspace_plan(lib):
+    # 2 x 4 heads: 8 (batch, head) pairs -> several L-segments; one segment needs no workspace
+    p = SP(seqlen=4096, segments=0)
+    nseg = _abi.ssd_plan_segments(p)
+    assert 1 < nseg <= 64
+    need = _abi.ssd_workspace_bytes(p)
+    assert need >= 8 * (nseg - 1) * 64 * 128 * 4
+    assert call_ssd(p) == 6                          # workspace missing
+    assert call_ssd(p, ws=FAKE, ws_bytes=need - 1) == 6
+    assert call_ssd(p, ws=FAKE + 4, ws_bytes=need) == 6   # misaligned
+    p1 = SP(seqlen=4096, segments=1)
+    assert _abi.ssd_plan_segments(p1) == 1 and _abi.ssd_workspace_bytes(p1) == 0
+    assert _abi.ssd_plan_segments(SP(seqlen=100, segments=50)) == 2   # clamped to the 64-step chunks
+    assert _abi.ssd_plan_segments(SP(batch=0)) == 0 and _abi.ssd_workspace_bytes(SP(batch=0)) == 0

@@ -30,11 +30,11 @@ def ref(d, disc=0, softplus=True, heads=None):
                       h0=f["h0"], disc=disc, softplus=softplus)
 
 
-def run(dd, disc=0, softplus=True, y_dtype=None, h0="given"):
+def run(dd, disc=0, softplus=True, y_dtype=None, h0="given", segments=0):
     torch = G.torch_dev()
     y, hf = ssm.ssd_fwd(dd["x"], dd["dt"], dd["A"], dd["B"], dd["C"], dt_bias=dd["dt_bias"], Dskip=dd["Dskip"],
                         z=dd["z"], h0=dd["h0"] if h0 == "given" else h0, disc=disc, softplus=softplus,
-                        y_dtype=torch.float32 if y_dtype is None else y_dtype)
+                        y_dtype=torch.float32 if y_dtype is None else y_dtype, segments=segments)
     torch.cuda.synchronize()
     return y, hf
 
@@ -61,6 +61,24 @@ def test_ssd_random(seed, b, L, H, Gr, N, disc, gate, dskip, h0, bias):
     # bf16 y is the round-to-nearest-even of the same fp32 result
     yb, _ = run(dd, disc=disc, y_dtype=torch.bfloat16)
     assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("disc", [0, 1])
+def test_ssd_segments(disc):
+    # L-segments: a zero-start pass per segment, then every segment from h0 carried through the ones before it.
+    # Each split must match the oracle and the single-segment run (11 chunks, the last one ragged).
+    torch = G.torch_dev()
+    d = I.random_small_ssd(13 + disc, 2, 700, 3, 64, 1, 128, h0=True)
+    dd = G.to_dev(d)
+    yr, hr = ref(d, disc=disc)
+    y1, h1 = run(dd, disc=disc, segments=1)
+    for k in (2, 3, 5, 11):
+        y, hf = run(dd, disc=disc, segments=k)
+        ey, eh = G.rel_max(G.to_np64(y), yr), G.rel_max(G.to_np64(hf), hr)
+        print("segments %d: y err %.2e, h err %.2e" % (k, ey, eh), flush=True)
+        assert ey <= TOL_SSD and eh <= TOL_SSD, (k, ey, eh)
+        assert G.rel_max(G.to_np64(y), G.to_np64(y1)) <= 1e-4, k
+    assert G.rel_max(G.to_np64(y1), yr) <= TOL_SSD
 
 
 def test_ssd_softplus_off():
