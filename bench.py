@@ -97,11 +97,20 @@ def ssd_algorithmic_flops(b, L, H, P, G, N, Q=64):
     return b * nc * (G * 2 * Q * Q * N + H * (Q * (Q + 1) * P + 4 * Q * N * P))
 
 
-def src_hash():
-    """Hash of every kernel source file: counter records taken on other sources are stale."""
+# the source files each kernel is built from (its translation unit and the headers it includes)
+KERNEL_SOURCES = (("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
+                  ("decode_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
+                  ("bwd_", ("common.hpp", "ssm_scan_bwd.hip")),
+                  ("ssd_", ("common.hpp", "ssm_ssd.hip")),
+                  ("complex_", ("common.hpp", "ssm_complex_scan.hip")))
+
+
+def src_hash(kernel_key):
+    """Hash of the sources a kernel is built from: a counter record taken on other sources is stale."""
+    files = next(f for prefix, f in KERNEL_SOURCES if kernel_key.startswith(prefix))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_57_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in files:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -120,7 +129,7 @@ def measured_traffic(kernel_key):
             continue
         f = [x.strip() for x in line.split("|")]
         if len(f) == 4 and f[0] == kernel_key:
-            if f[1] != src_hash():
+            if f[1] != src_hash(kernel_key):
                 return None
             return int(f[2]) + int(f[3])
     return None
