@@ -105,6 +105,13 @@ KERNEL_SOURCES = (("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")
                   ("complex_", ("common.hpp", "ssm_complex_scan.hip")))
 
 
+def ssd_decode_algorithmic_bytes(b, H, P, G, N, io_bytes=2, gate=True):
+    """One SSD decode step: the fp32 state read and written, x (and z) read and y written, dt, B, C, per-head
+    parameters."""
+    return (2 * b * H * P * N * 4 + b * H * P * io_bytes * (3 if gate else 2) + b * H * io_bytes
+            + 2 * b * G * N * io_bytes + 3 * H * 4)
+
+
 def src_hash(kernel_key):
     """Hash of the sources a kernel is built from: a counter record taken on other sources is stale."""
     files = next(f for prefix, f in KERNEL_SOURCES if kernel_key.startswith(prefix))
@@ -363,6 +370,57 @@ def main():
                                    "algorithmic_bytes": sby},
                       "mfma": {"algorithmic_flops": sfl, "achieved_TFLOPs": stf, "peak_bf16_TFLOPs": 2500.0,
                                "frac": stf / 2500.0}}
+        if not args.no_cpu_baseline:
+            # the fp64 SSD oracle on a bounded sample of the same inputs: batch element 0, all heads and steps
+            import oracle
+            oracle.build(force=False)
+            fs = I.as_f64({k: (None if v is None else (v[:1] if k in ("x", "z", "dt", "B", "C") else v))
+                           for k, v in hs.items()})
+            t0 = time.perf_counter()
+            oracle.ssd(fs["x"], fs["dt"], fs["A"], fs["B"], fs["C"], dt_bias=fs["dt_bias"], Dskip=fs["Dskip"],
+                       z=fs["z"], nthreads=host_cores())
+            cs = time.perf_counter() - t0
+            out["ssd"]["cpu_baseline"] = {"value": sL * sH * sP / cs, "unit": "elements/s", "cores": host_cores(),
+                                          "kind": "oracle", "seconds": cs,
+                                          "sample": "batch element 0 of the layer (1/4 of it), fp64"}
+        del sd, ys, hfs, sws
+
+    # ---- Mamba-2 SSD decode: 8 single-token steps with fresh inputs (256 sequences, 80 heads of 64, N = 128)
+    if not args.no_ssd and not args.no_decode:
+        from selective_state_space_57_amd import _abi
+        wsd = I.SSD_WORKLOADS[2]
+        db_, dH, dP, dG, dN = wsd.batch, wsd.nheads, wsd.headdim, wsd.ngroups, wsd.dstate
+        sstate = torch.from_numpy(I.ssd_inputs(wsd, with_h0=True)["h0"]).to(dev)
+        sin = [{k: up(v) for k, v in I.ssd_inputs(wsd, step=s_).items() if k != "h0"} for s_ in range(wsd.decode_steps)]
+        ysd = torch.empty((db_, dH, dP), dtype=torch.bfloat16, device=dev)
+        pdd = _abi.make_ssd_params(db_, 1, dH, dP, dG, dN, ssm.SSM_BF16, ssm.SSM_BF16)
+        sdargs = [(sstate.data_ptr(), q["x"].data_ptr(), q["dt"].data_ptr(), q["dt_bias"].data_ptr(),
+                   q["A"].data_ptr(), q["B"].data_ptr(), q["C"].data_ptr(), q["Dskip"].data_ptr(), q["z"].data_ptr(),
+                   ysd.data_ptr(), stream.cuda_stream) for q in sin]
+
+        def sdstep(s_):
+            st = _abi.ssd_state_update_raw(pdd, *sdargs[s_])
+            if st:
+                _abi.check(st)
+
+        for s_ in range(2):
+            sdstep(s_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s_ in range(wsd.decode_steps):
+            sdstep(s_)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sdms = e0.elapsed_time(e1) / wsd.decode_steps
+        sdby = ssd_decode_algorithmic_bytes(db_, dH, dP, dG, dN)
+        out["ssd_decode"] = {"workload": "mamba2-decode-b256: 256 sequences, 80 heads x 64, N = 128, bf16 io",
+                             "steps": wsd.decode_steps, "us_per_step": sdms * 1e3,
+                             "roofline": {"bound": "hbm", "achieved": sdby / (sdms * 1e-3) / 1e9,
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": sdby / (sdms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                          "algorithmic_bytes": sdby}}
+        del sstate, sin
 
     # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
     if not args.no_bwd:

@@ -495,7 +495,7 @@ ssd_fwd_kernel(SsdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------------------
-// decode step: one thread per (b, h, p, 4 consecutive n); a row of N/4 threads reduces C . S across its lanes.
+// decode step
 
 struct SsdDecodeArgs {
   float* state;
@@ -513,13 +513,15 @@ struct SsdDecodeArgs {
   int softplus;
 };
 
+// A state row (one (b, h, p)) of N fp32 values is owned by 16 lanes: lane q holds the 16-byte pieces q + 16 i
+// (i < N / 64), so each load instruction covers 256 contiguous bytes of a row; C . S is summed over the 16 lanes by
+// DPP rotations within the row.  Four rows per wave, 16 rows per workgroup.
 template <int N, typename TY, bool ZOH>
 __global__ void __launch_bounds__(256) ssd_decode_kernel(SsdDecodeArgs a) {
-  constexpr int TPR = N / 4;           // threads per state row (16, 32 or 64)
-  constexpr int RPB = 256 / TPR;       // rows per block
+  constexpr int kV = N / 64;           // 16-byte pieces per lane
   const int tid = threadIdx.x;
-  const int64_t row = int64_t(blockIdx.x) * RPB + tid / TPR;
-  const int q = tid % TPR;
+  const int64_t row = int64_t(blockIdx.x) * 16 + tid / 16;
+  const int q = tid % 16;
   const bool live = row < a.rows;
   const int64_t r = live ? row : 0;
   const int64_t bh = r / a.P;          // b * H + h
@@ -534,21 +536,35 @@ __global__ void __launch_bounds__(256) ssd_decode_kernel(SsdDecodeArgs a) {
   const float ph = ZOH ? (Ah == 0.0f ? dl : expm1_from(e, abar) / Ah) : dl;
   const float xv = bf_lo(a.x[r]);
   const float bx = ph * xv;
-  const int64_t bc = (b * a.G + g) * N + 4 * q;
-  const uint2 bw = *reinterpret_cast<const uint2*>(a.B + bc);
-  const uint2 cw = *reinterpret_cast<const uint2*>(a.C + bc);
-  f4 s = live ? *reinterpret_cast<const f4*>(a.state + r * N + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
-  const float bv[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
-  const float cv[4] = {bf_lo(cw.x), bf_hi(cw.x), bf_lo(cw.y), bf_hi(cw.y)};
+  const uint16_t* Bt = a.B + (b * a.G + g) * N;
+  const uint16_t* Ct = a.C + (b * a.G + g) * N;
+  float* srow = a.state + r * N;
+  f4 s[kV];
+  uint2 bw[kV], cw[kV];
+#pragma unroll
+  for (int i = 0; i < kV; ++i) {
+    const int n0 = 4 * (q + 16 * i);
+    s[i] = live ? *reinterpret_cast<const f4*>(srow + n0) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    bw[i] = *reinterpret_cast<const uint2*>(Bt + n0);
+    cw[i] = *reinterpret_cast<const uint2*>(Ct + n0);
+  }
   float acc = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    s[c] = fmaf(abar, s[c], bx * bv[c]);
-    acc = fmaf(cv[c], s[c], acc);
-  }
-  if (live) *reinterpret_cast<f4*>(a.state + r * N + 4 * q) = s;
+  for (int i = 0; i < kV; ++i) {
+    const float bv[4] = {bf_lo(bw[i].x), bf_hi(bw[i].x), bf_lo(bw[i].y), bf_hi(bw[i].y)};
+    const float cv[4] = {bf_lo(cw[i].x), bf_hi(cw[i].x), bf_lo(cw[i].y), bf_hi(cw[i].y)};
 #pragma unroll
-  for (int d = TPR / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, TPR);
+    for (int c = 0; c < 4; ++c) {
+      s[i][c] = fmaf(abar, s[i][c], bx * bv[c]);
+      acc = fmaf(cv[c], s[i][c], acc);
+    }
+    if (live) *reinterpret_cast<f4*>(srow + 4 * (q + 16 * i)) = s[i];
+  }
+  // sum over the 16 lanes of the row: rotations by 8, 4, 2, 1 leave the total in every lane
+  acc += row_ror<8>(acc);
+  acc += row_ror<4>(acc);
+  acc += row_ror<2>(acc);
+  acc += row_ror<1>(acc);
   if (live && q == 0) {
     float yv = acc;
     if (a.Dskip) yv = fmaf(a.Dskip[h], xv, yv);
@@ -643,7 +659,7 @@ SsdPlan ssd_plan(const ssm_ssd_params* p) {
 
 template <int N, typename TY>
 ssm_status launch_decode(const SsdDecodeArgs& a, bool zoh, hipStream_t st) {
-  constexpr int RPB = 256 / (N / 4);
+  constexpr int RPB = 16;
   const int64_t blocks = (a.rows + RPB - 1) / RPB;
   if (blocks >= (int64_t(1) << 31)) return fail(SSM_ERR_SHAPE, "too many rows for one launch");
   if (zoh)

@@ -106,6 +106,7 @@ class SSDWorkload:
 SSD_WORKLOADS = {
     0: SSDWorkload("tiny-ssd", 1, 200, 4, 64, 1, 128, BF16, 1e-3, 1e-1, cfg_id=100),
     1: SSDWorkload("mamba2-2.7b-layer", 4, 4096, 80, 64, 1, 128, BF16, 1e-3, 1e-1, cfg_id=101),
+    2: SSDWorkload("mamba2-decode-b256", 256, 1, 80, 64, 1, 128, BF16, 1e-3, 1e-1, decode_steps=8, cfg_id=102),
 }
 
 
