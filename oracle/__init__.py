@@ -57,6 +57,8 @@ def _bind(path: str):
     lib.oracle_scan_bwd_f64.restype = I
     lib.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 6 + [I]
     lib.oracle_conv1d_f64.restype = I
+    lib.oracle_conv1d_bwd_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 10 + [I]
+    lib.oracle_conv1d_bwd_f64.restype = I
     lib.oracle_complex_scan_f64.argtypes = [I64, I64, I64, I64, I, I] + [P] * 11 + [I]
     lib.oracle_complex_scan_f64.restype = I
     lib.oracle_complex_state_update_f64.argtypes = [I64, I64, I64, I, I] + [P] * 10
@@ -207,6 +209,24 @@ def conv1d(x, w, bias=None, state_in=None, silu=True, nthreads=0, _lib_override=
     return u, st
 
 
+def conv1d_bwd(x, w, du, bias=None, state_in=None, dstate_out=None, silu=True, nthreads=0, _lib_override=None):
+    """Backward of conv1d: returns dict dx (b, D, L), dw (D, K), dbias (D,), dstate_in (b, D, K-1) for the loss
+    sum(du * u) + sum(dstate_out * state_out)."""
+    x = _f64(x)
+    bsz, dim, L = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    out = {"dx": np.zeros((bsz, dim, L)), "dw": np.zeros((dim, K)), "dbias": np.zeros(dim),
+           "dstate_in": np.zeros((bsz, dim, K - 1))}
+    rc = (_lib_override or _load()).oracle_conv1d_bwd_f64(
+        bsz, dim, L, K, int(bool(silu)), _ptr(x), _ptr(w), _ptr(_f64(bias, (dim,))), _ptr(_f64(state_in, (bsz, dim, K - 1))),
+        _ptr(_f64(du, (bsz, dim, L))), _ptr(_f64(dstate_out, (bsz, dim, K - 1))), _ptr(out["dx"]), _ptr(out["dw"]),
+        _ptr(out["dbias"]), _ptr(out["dstate_in"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_conv1d_bwd_f64 failed with code %d" % rc)
+    return out
+
+
 def complex_scan(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, disc=EULER_B, softplus=True, nthreads=0,
                  _lib_override=None):
     """Complex diagonal A: A (D, N) complex, B, C (b, N, L) complex, h0 (b, D, N) complex (numpy complex arrays or
@@ -306,6 +326,9 @@ class Oracle:
 
     def conv1d(self, *a, **k):
         return conv1d(*a, _lib_override=self._lib, **k)
+
+    def conv1d_bwd(self, *a, **k):
+        return conv1d_bwd(*a, _lib_override=self._lib, **k)
 
     def complex_scan(self, *a, **k):
         return complex_scan(*a, _lib_override=self._lib, **k)

@@ -332,6 +332,71 @@ int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
 }
 
 /*
+ * Backward of oracle_conv1d_f64: the chain rule through u_t = act(pre_t), pre_t = bias + sum_k w[k] e[t + k], where e
+ * is the extended input (the K-1 window values of state_in, oldest first, then x).  Given du = dL/du and, optionally,
+ * dstate_out = dL/d(state_out) (state_out holds e[L .. L+K-2]):
+ *   dpre_t     = du_t act'(pre_t)          act' of SiLU = s (1 + pre (1 - s)) with s = sigmoid(pre); 1 without
+ *   de[t + k] += w[k] dpre_t,   de[L + i] += dstate_out[i]
+ *   dx[t] = de[K-1 + t],  dstate_in[j] = de[j],  dw[d][k] = sum_b sum_t dpre_t e[t + k],  dbias[d] = sum_b sum_t dpre_t
+ * Outputs are overwritten; dbias and dstate_in may be NULL.
+ */
+int oracle_conv1d_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int use_silu, const double* x,
+                          const double* w, const double* bias, const double* state_in, const double* du,
+                          const double* dstate_out, double* dx, double* dw, double* dbias, double* dstate_in,
+                          int nthreads) {
+  if (batch < 0 || dim < 0 || seqlen < 1 || width < 1 || width > 64) return 1;
+  if (!x || !w || !du || !dx || !dw) return 2;
+  const int64_t K = width, S = width - 1, L = seqlen;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t d = 0; d < dim; ++d) {
+    double* e = (double*)malloc(sizeof(double) * (size_t)(S + L));
+    double* de = (double*)malloc(sizeof(double) * (size_t)(S + L));
+    if (!e || !de) {
+#pragma omp atomic write
+      failed = 1;
+      free(e); free(de);
+      continue;
+    }
+    double sw[64] = {0.0}, sb = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      const int64_t bd = b * dim + d;
+      for (int64_t j = 0; j < S; ++j) e[j] = state_in ? state_in[bd * S + j] : 0.0;
+      for (int64_t t = 0; t < L; ++t) e[S + t] = x[bd * L + t];
+      for (int64_t i = 0; i < S + L; ++i) de[i] = 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        double pre = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) pre += w[d * K + k] * e[t + k];
+        double g = du[bd * L + t];
+        if (use_silu) {
+          const double sg = 1.0 / (1.0 + exp(-pre));
+          g *= sg * (1.0 + pre * (1.0 - sg));
+        }
+        for (int64_t k = 0; k < K; ++k) {
+          de[t + k] += w[d * K + k] * g;
+          sw[k] += g * e[t + k];
+        }
+        sb += g;
+      }
+      if (dstate_out)
+        for (int64_t i = 0; i < S; ++i) de[L + i] += dstate_out[bd * S + i];
+      for (int64_t t = 0; t < L; ++t) dx[bd * L + t] = de[S + t];
+      if (dstate_in)
+        for (int64_t j = 0; j < S; ++j) dstate_in[bd * S + j] = de[j];
+    }
+    for (int64_t k = 0; k < K; ++k) dw[d * K + k] = sw[k];
+    if (dbias) dbias[d] = sb;
+    free(e); free(de);
+  }
+  return failed ? 3 : 0;
+}
+
+/*
  * Complex diagonal A (test infrastructure, fp64).  The Mamba paper (section 3.6, "real vs. complex") keeps a complex
  * state for continuous modalities and initialises A with S4D-Lin, A_n = -1/2 + n i (audio experiments, section 4.4).
  * Same recurrence as oracle_scan_f64 in complex arithmetic, with B and C complex and a real output:

@@ -373,6 +373,43 @@ def pin_conv_split(orc, seed=12):
 #      (brute force), both rules; (c) conjugating A, B, C, h0 leaves y unchanged and conjugates h_final; (d) an
 #      impulse through a pure rotation (A = i w, N = 1, Delta = dt fixed): y_t = Delta cos(w Delta t); (e) L decode
 #      steps = one scan.
+def pin_conv_bwd_finite_differences(orc, seed=15):
+    """Backward of the causal convolution (+ SiLU) = central differences of the (pinned) forward, element by element,
+    for x, the taps, the bias and the incoming window, loss sum(du u) + sum(dstate_out state_out); also a sequence
+    shorter than the window (the returned window then still holds part of the incoming one)."""
+    r = _rng(seed)
+    for (b, D, L, K, silu) in ((2, 3, 11, 4, True), (1, 2, 9, 3, False), (2, 2, 2, 4, True), (1, 3, 6, 1, True)):
+        x = r.standard_normal((b, D, L))
+        w = r.standard_normal((D, K)) * 0.7
+        bias = r.standard_normal(D)
+        st = r.standard_normal((b, D, K - 1))
+        du = r.standard_normal((b, D, L))
+        dso = r.standard_normal((b, D, K - 1))
+        g = orc.conv1d_bwd(x, w, du, bias=bias, state_in=st, dstate_out=dso, silu=silu)
+
+        def loss(x_, w_, b_, s_):
+            u, so = orc.conv1d(x_, w_, b_, s_, silu=silu)
+            return float(np.sum(u * du) + np.sum(so * dso))
+
+        eps = 1e-6
+        for name, arr, key in (("x", x, "dx"), ("w", w, "dw"), ("bias", bias, "dbias"), ("state", st, "dstate_in")):
+            if arr.size == 0:
+                continue
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                args = {"x": x, "w": w, "bias": bias, "state": st}
+                ap, am = arr.copy(), arr.copy()
+                ap[idx] += eps
+                am[idx] -= eps
+                args[name] = ap
+                lp = loss(args["x"], args["w"], args["bias"], args["state"])
+                args[name] = am
+                lm = loss(args["x"], args["w"], args["bias"], args["state"])
+                num[idx] = (lp - lm) / (2 * eps)
+            err = float(np.max(np.abs(num - g[key]))) / max(1.0, float(np.max(np.abs(num))))
+            assert err < 1e-7, ("conv bwd", name, b, D, L, K, silu, err)
+
+
 def pin_complex(orc, seed=13):
     r = _rng(seed)
     b, D, L, N = 2, 3, 24, 4
@@ -532,6 +569,7 @@ def all_pins(orc, worked_rows):
                    ("decode_scan_%d" % disc, lambda disc=disc: pin_decode_scan(orc, disc)),
                    ("bwd_fd_%d" % disc, lambda disc=disc: pin_bwd_finite_differences(orc, disc))]
     checks += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
+               ("conv_bwd_fd", lambda: pin_conv_bwd_finite_differences(orc)),
                ("complex", lambda: pin_complex(orc)), ("ssd", lambda: pin_ssd(orc))]
     for name, fn in checks:
         try:

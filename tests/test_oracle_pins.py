@@ -81,6 +81,10 @@ def test_conv_numpy(orc):
     pins.pin_conv_numpy(orc)
 
 
+def test_conv_backward_finite_differences(orc):
+    pins.pin_conv_bwd_finite_differences(orc)
+
+
 def test_conv_split(orc):
     pins.pin_conv_split(orc)
 
@@ -111,8 +115,8 @@ def test_all_pins_run_and_pass(orc):
     res = pins.all_pins(orc, load_worked())
     assert all(isinstance(k, str) and e is None for k, e in res), [r for r in res if r[1] is not None]
     names = {k for k, _ in res}
-    for must in ("worked", "theorem1", "zoh_euler", "split_0", "bwd_fd_1", "conv_numpy", "conv_split", "complex",
-                 "ssd"):
+    for must in ("worked", "theorem1", "zoh_euler", "split_0", "bwd_fd_1", "conv_numpy", "conv_split", "conv_bwd_fd",
+                 "complex", "ssd"):
         assert must in names, must
 
 
@@ -155,6 +159,11 @@ MUTANTS = [
     ("complex_output_sign", r"y \+= Ct\[n \* bstride\] \* h\[2 \* n\] - Ct", "y += Ct[n * bstride] * h[2 * n] + Ct"),
     ("complex_zoh_division", r"ci = \(ei \* ar - er \* ai\) / den;", "ci = (ei * ar + er * ai) / den;"),
     ("complex_cos_sin_swapped", r"abr = mag \* cos\(ang\), abi = mag \* sin\(ang\)", "abr = mag * sin(ang), abi = mag * cos(ang)"),
+    ("conv_bwd_silu_derivative", r"g \*= sg \* \(1\.0 \+ pre \* \(1\.0 - sg\)\);", "g *= sg;"),
+    ("conv_bwd_window_out_ignored", r"for \(int64_t i = 0; i < S; \+\+i\) de\[L \+ i\] \+= dstate_out\[bd \* S \+ i\];",
+     "for (int64_t i = 0; i < S; ++i) de[L + i] += 0.0;"),
+    ("conv_bwd_taps_flipped", r"de\[t \+ k\] \+= w\[d \* K \+ k\] \* g;", "de[t + k] += w[d * K + (K - 1 - k)] * g;"),
+    ("conv_bwd_dw_shift", r"sw\[k\] \+= g \* e\[t \+ k\];", "sw[k] += g * e[t + (k > 0 ? k - 1 : 0)];"),
     ("ssd_group_index", r"g = h / hpg", "g = h % G"),
     ("ssd_abar_sign", r"const double abar = exp\(delta \* Ah\);", "const double abar = exp(-delta * Ah);"),
     ("ssd_euler_no_delta", r"coef = disc == 0 \? delta :", "coef = disc == 0 ? 1.0 :"),
