@@ -288,6 +288,39 @@ def main():
                             "algorithmic_bytes": nbytes + D * 4 * 5,
                             "note": "x is read once and the convolved sequence never goes to memory; a separate "
                                     "convolution kernel would add a write and a read of it (2 x 168 MB in bf16)"}
+        # the convolution on its own (recompute of u for training) and its backward, bf16 in and out
+        uu = torch.empty((b, D, L), dtype=torch.bfloat16, device=dev)
+        gdx = torch.empty((b, D, L), dtype=torch.bfloat16, device=dev)
+        gdw = torch.empty((D, 4), dtype=torch.float32, device=dev)
+        gdb = torch.empty((D,), dtype=torch.float32, device=dev)
+
+        def kfwd():
+            _abi.check(_abi.conv1d_fwd_raw(p, conv, d["x"].data_ptr(), uu.data_ptr(), stream.cuda_stream))
+
+        def kbwd():
+            _abi.check(_abi.conv1d_bwd_raw(p, conv, d["x"].data_ptr(), uu.data_ptr(), 0, gdx.data_ptr(),
+                                           gdw.data_ptr(), gdb.data_ptr(), 0, stream.cuda_stream))
+
+        ctimes = {}
+        for name, fn in (("fwd", kfwd), ("bwd", kbwd)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ctimes[name] = e0.elapsed_time(e1) / args.steps
+        cby = {"fwd": 2 * elems * 2, "bwd": 3 * elems * 2}   # x read + u written; x, du read + dx written (bf16)
+        for name in ("fwd", "bwd"):
+            gbs_ = cby[name] / (ctimes[name] * 1e-3) / 1e9
+            out["conv_scan"]["conv1d_" + name] = {
+                "ms": ctimes[name], "algorithmic_bytes": cby[name],
+                "roofline": {"bound": "hbm", "achieved": gbs_, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs_ / HBM_PEAK_GBS}}
+        del uu, gdx
 
     # ---- complex diagonal A (S4D-Lin) on the same shape: complex B, C and state
     if not args.no_complex:

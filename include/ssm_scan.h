@@ -141,6 +141,26 @@ ssm_status ssm_conv_state_update(const ssm_scan_params* p, const ssm_conv_params
                                  const float* Dskip, const void* z, void* y, void* stream);
 
 /*
+ * The convolution above on its own, for training: u = act(bias + sum_k weight[k] x_{t-(width-1)+k}) with the inputs
+ * before t = 0 from conv->state_in (conv->state_out is ignored).  A backward pass calls it to recompute u for
+ * ssm_scan_bwd (which returns dL/du as its dx), then ssm_conv1d_bwd.  x [batch][dim][seqlen] io_dtype, u the same
+ * shape in y_dtype.  p->dstate, disc and dt_softplus are validated as for the scan and otherwise unused.
+ */
+ssm_status ssm_conv1d_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, const void* x, void* u,
+                          void* stream);
+
+/*
+ * Backward of the convolution (+ activation): the chain rule through u above for the loss whose gradient is
+ * du = dL/du [batch][dim][seqlen] y_dtype and, optionally, dstate_out = dL/d(conv->state_out) [batch][dim][width-1]
+ * fp32 (the returned window).  Outputs (overwritten): dx [batch][dim][seqlen] y_dtype;  dweight [dim][width] fp32
+ * (summed over batch and time, required);  dbias [dim] fp32 and dstate_in [batch][dim][width-1] fp32 (the incoming
+ * window's gradient), each optional.  x, conv->weight, bias and state_in as given to the forward.  Deterministic.
+ */
+ssm_status ssm_conv1d_bwd(const ssm_scan_params* p, const ssm_conv_params* conv, const void* x, const void* du,
+                          const float* dstate_out, void* dx, float* dweight, float* dbias, float* dstate_in,
+                          void* stream);
+
+/*
  * Scan with a complex diagonal A (Mamba paper section 3.6 "real vs. complex", S4D-Lin initialisation A_n = -1/2 + n i,
  * used for continuous modalities such as audio, section 4.4).  The state is complex and so are B and C; the output
  * is real:  Abar = exp(Delta A),  Bbar = Delta B (SSM_DISC_EULER_B) or (exp(Delta A) - 1) / A * B (SSM_DISC_ZOH; A = 0

@@ -14,7 +14,7 @@ from ._abi import (EULER_B, ZOH, SSM_BF16, SSM_F32, SSMError, Params, make_param
                    bwd_workspace_bytes)
 
 __all__ = ["scan_fwd", "scan_bwd", "state_update", "conv_scan_fwd", "conv_state_update", "complex_scan_fwd",
-           "complex_state_update", "ssd_fwd", "ssd_state_update", "ssd_workspace_bytes", "EULER_B", "ZOH", "SSMError",
+           "complex_state_update", "conv1d_fwd", "conv1d_bwd", "ssd_fwd", "ssd_state_update", "ssd_workspace_bytes", "EULER_B", "ZOH", "SSMError",
            "Params", "make_params", "workspace_bytes", "bwd_workspace_bytes", "plan_segments", "io_code"]
 
 
@@ -232,6 +232,51 @@ def conv_state_update(state, conv_state, x, conv_w, dt, A, B, C, dt_bias=None, D
                                     _addr(C), _addr(Dskip), _addr(z), _addr(y), _stream_handle(stream, dev))
     _abi.check(st)
     return y
+
+
+def conv1d_fwd(x, conv_w, conv_bias=None, conv_state=None, *, activation=True, u=None, u_dtype=None, stream=None):
+    """The causal depthwise convolution (+ SiLU) alone: x (b, D, L) -> u (b, D, L) (dtype u_dtype, default x's);
+    conv_w (D, width) float32, conv_bias (D,), conv_state (b, D, width-1) float32: the inputs before t = 0."""
+    import torch
+    b, D, L = x.shape
+    io = io_code(x.dtype)
+    udt = _out_dtype(u, u_dtype, x.dtype)
+    dev = x.device
+    _expect("x", x, (b, D, L), x.dtype, dev, optional=False)
+    _expect("u", u, (b, D, L), udt, dev)
+    conv = _conv_params(conv_w, conv_bias, conv_state, None, activation, D, b, dev)
+    p = make_params(b, D, L, 16, io, io_code(udt))
+    if u is None:
+        u = torch.empty((b, D, L), dtype=udt, device=dev)
+    _abi.check(_abi.conv1d_fwd_raw(p, conv, _addr(x), _addr(u), _stream_handle(stream, dev)))
+    return u
+
+
+def conv1d_bwd(x, conv_w, du, conv_bias=None, conv_state=None, dstate_out=None, *, activation=True, dx=None,
+               stream=None):
+    """Backward of conv1d_fwd for dL/du = du (b, D, L) (dtype of dx) and optionally dL/d(returned window)
+    dstate_out (b, D, width-1) float32.  Returns dict dx (b, D, L), dweight (D, width), dbias (D,), dstate_in
+    (b, D, width-1)."""
+    import torch
+    b, D, L = x.shape
+    io = io_code(x.dtype)
+    gdt = du.dtype
+    dev = x.device
+    f32 = torch.float32
+    _expect("x", x, (b, D, L), x.dtype, dev, optional=False)
+    _expect("du", du, (b, D, L), gdt, dev, optional=False)
+    _expect("dx", dx, (b, D, L), gdt, dev)
+    conv = _conv_params(conv_w, conv_bias, conv_state, None, activation, D, b, dev)
+    K = conv_w.shape[1]
+    _expect("dstate_out", dstate_out, (b, D, K - 1), f32, dev)
+    p = make_params(b, D, L, 16, io, io_code(gdt))
+    out = {"dx": dx if dx is not None else torch.empty((b, D, L), dtype=gdt, device=dev),
+           "dweight": torch.empty((D, K), dtype=f32, device=dev), "dbias": torch.empty((D,), dtype=f32, device=dev),
+           "dstate_in": torch.empty((b, D, K - 1), dtype=f32, device=dev)}
+    _abi.check(_abi.conv1d_bwd_raw(p, conv, _addr(x), _addr(du), _addr(dstate_out), _addr(out["dx"]),
+                                   _addr(out["dweight"]), _addr(out["dbias"]),
+                                   _addr(out["dstate_in"]) if K > 1 else 0, _stream_handle(stream, dev)))
+    return out
 
 
 def complex_scan_fwd(x, dt, A, B, C, dt_bias=None, Dskip=None, z=None, h0=None, *, y=None, h_final=None,

@@ -18,7 +18,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE"
 EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "ssm_status_str", "ssm_last_error",
            "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update",
-           "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan_segments"]
+           "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan_segments",
+           "ssm_conv1d_fwd", "ssm_conv1d_bwd"]
 
 
 class Params(ctypes.Structure):
@@ -77,6 +78,10 @@ def lib():
         L.ssm_conv_scan_fwd.restype = ctypes.c_int
         L.ssm_conv_state_update.argtypes = [PP, CP] + [P] * 11
         L.ssm_conv_state_update.restype = ctypes.c_int
+        L.ssm_conv1d_fwd.argtypes = [PP, CP, P, P, P]
+        L.ssm_conv1d_fwd.restype = ctypes.c_int
+        L.ssm_conv1d_bwd.argtypes = [PP, CP] + [P] * 8
+        L.ssm_conv1d_bwd.restype = ctypes.c_int
         L.ssm_complex_scan_fwd.argtypes = [PP] + [P] * 12
         L.ssm_complex_scan_fwd.restype = ctypes.c_int
         L.ssm_complex_state_update.argtypes = [PP] + [P] * 11
@@ -161,6 +166,15 @@ def conv_scan_fwd_raw(p: Params, conv: ConvParams, x, dt, dt_bias, A, B, C, Dski
 def conv_state_update_raw(p: Params, conv: ConvParams, state, x, dt, dt_bias, A, B, C, Dskip, z, y, stream):
     return lib().ssm_conv_state_update(ctypes.byref(p), ctypes.byref(conv), state, x, dt, dt_bias, A, B, C, Dskip, z,
                                        y, stream)
+
+
+def conv1d_fwd_raw(p: Params, conv: ConvParams, x, u, stream):
+    return lib().ssm_conv1d_fwd(ctypes.byref(p), ctypes.byref(conv), x, u, stream)
+
+
+def conv1d_bwd_raw(p: Params, conv: ConvParams, x, du, dstate_out, dx, dweight, dbias, dstate_in, stream):
+    return lib().ssm_conv1d_bwd(ctypes.byref(p), ctypes.byref(conv), x, du, dstate_out, dx, dweight, dbias, dstate_in,
+                                stream)
 
 
 def complex_scan_fwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream):

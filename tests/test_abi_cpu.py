@@ -212,3 +212,20 @@ def test_ssd_workspace_plan(lib):
     assert _abi.ssd_plan_segments(p1) == 1 and _abi.ssd_workspace_bytes(p1) == 0
     assert _abi.ssd_plan_segments(SP(seqlen=100, segments=50)) == 2   # clamped to the 64-step chunks
     assert _abi.ssd_plan_segments(SP(batch=0)) == 0 and _abi.ssd_workspace_bytes(SP(batch=0)) == 0
+
+
+def test_conv1d_entry_point_errors(lib):
+    conv = _abi.make_conv(FAKE, 4)
+    assert _abi.conv1d_fwd_raw(P(), conv, 0, FAKE, 0) == 1
+    assert _abi.conv1d_fwd_raw(P(), conv, FAKE, 0, 0) == 1
+    assert _abi.conv1d_fwd_raw(P(), _abi.make_conv(FAKE, 5), FAKE, FAKE, 0) == 4
+    assert _abi.conv1d_fwd_raw(P(), _abi.make_conv(0, 4), FAKE, FAKE, 0) == 1
+    assert _abi.conv1d_fwd_raw(P(batch=0), conv, FAKE, FAKE, 0) == 2
+    assert _abi.conv1d_fwd_raw(P(), conv, FAKE + 1, FAKE, 0) == 5
+    # backward: x, du, dx and dweight required
+    for missing in range(4):
+        args = [FAKE, FAKE, 0, FAKE, FAKE, 0, 0]
+        args[[0, 1, 3, 4][missing]] = 0
+        assert _abi.conv1d_bwd_raw(P(), conv, *args, 0) == 1
+    assert _abi.conv1d_bwd_raw(P(), conv, FAKE, FAKE, 0, FAKE, FAKE + 2, 0, 0, 0) == 5
+    assert lib.ssm_last_error().decode()

@@ -132,3 +132,74 @@ def test_conv_scan_full_size_sampled():
         yr, _, _ = ref_conv_scan(sub, scv)
         ref.append(yr[0, 0])
     assert G.rel_max(got, np.stack(ref)) <= G.TOL_BF16
+
+
+# ---- the convolution on its own (recompute for training) and its backward
+
+@pytest.mark.parametrize("seed,b,D,L,io,width,state,silu", [
+    (21, 2, 17, 100, "f32", 4, True, True),
+    (22, 1, 9, 2, "f32", 4, True, True),        # shorter than the window
+    (23, 3, 12, 77, "bf16", 3, False, True),
+    (24, 2, 8, 130, "f32", 1, False, False),    # width 1, no activation
+    (25, 2, 64, 1000, "bf16", 4, True, True),
+])
+def test_conv1d_fwd_and_bwd(seed, b, D, L, io, width, state, silu):
+    torch = G.torch_dev()
+    d = I.random_small(seed, b, D, L, 16, io=io)
+    cv = I.random_small_conv(seed, b, D, 16, width=width, with_state=state)
+    cots = I.random_small_cotangents(seed, b, D, L, 16, io="f32")
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    f = I.as_f64(d)
+    st = None if cv["conv_state"] is None else cv["conv_state"].astype(np.float64)
+    w64, b64 = cv["conv_w"].astype(np.float64), cv["conv_b"].astype(np.float64)
+    # forward
+    u = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], dc["conv_state"], activation=silu, u_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ur, _ = oracle.conv1d(f["x"], w64, bias=b64, state_in=st, silu=silu)
+    assert G.rel_max(G.to_np64(u), ur) <= 1e-6
+    # backward, with a gradient for the returned window too
+    du = torch.from_numpy(cots["dy"]).cuda()
+    dso = (torch.from_numpy(np.random.default_rng(seed).standard_normal((b, D, width - 1)).astype(np.float32)).cuda()
+           if width > 1 else None)
+    g = ssm.conv1d_bwd(dd["x"], dc["conv_w"], du, dc["conv_b"], dc["conv_state"], dso, activation=silu)
+    torch.cuda.synchronize()
+    gr = oracle.conv1d_bwd(f["x"], w64, cots["dy"].astype(np.float64), bias=b64, state_in=st,
+                           dstate_out=None if dso is None else dso.cpu().numpy().astype(np.float64), silu=silu)
+    for k, tol in (("dx", 1e-5), ("dweight", 1e-5), ("dbias", 1e-5), ("dstate_in", 1e-5)):
+        rk = {"dweight": "dw"}.get(k, k)
+        if gr[rk].size == 0:
+            continue
+        e = G.rel_max(G.to_np64(g[k]), gr[rk])
+        assert e <= tol, (k, e)
+    # deterministic
+    g2 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], du, dc["conv_b"], dc["conv_state"], dso, activation=silu)
+    torch.cuda.synchronize()
+    assert all(torch.equal(g[k], g2[k]) for k in g)
+
+
+def test_conv_scan_training_chain():
+    # forward through the fused convolution + scan; backward: recompute u, scan backward (dL/du), convolution backward.
+    # Against the oracle composition: conv1d -> scan_bwd on its output -> conv1d_bwd.
+    torch = G.torch_dev()
+    b, D, L, N, width = 2, 24, 300, 16, 4
+    d = I.random_small(31, b, D, L, N, io="f32", h0=True)
+    cv = I.random_small_conv(31, b, D, N, width=width, with_state=True)
+    cots = I.random_small_cotangents(31, b, D, L, N, io="f32", dh_final=True)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    u = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], dc["conv_state"], u_dtype=torch.float32)
+    dy, dhf = torch.from_numpy(cots["dy"]).cuda(), torch.from_numpy(cots["dh_final"]).cuda()
+    gs = ssm.scan_bwd(u, dd["dt"], dd["A"], dd["B"], dd["C"], dy, dt_bias=dd["dt_bias"], Dskip=dd["Dskip"],
+                      z=dd["z"], h0=dd["h0"], dh_final=dhf)
+    gc = ssm.conv1d_bwd(dd["x"], dc["conv_w"], gs["dx"], dc["conv_b"], dc["conv_state"])
+    torch.cuda.synchronize()
+    f = I.as_f64(d)
+    w64, b64, st = (cv["conv_w"].astype(np.float64), cv["conv_b"].astype(np.float64),
+                    cv["conv_state"].astype(np.float64))
+    ur, _ = oracle.conv1d(f["x"], w64, bias=b64, state_in=st)
+    gsr = oracle.scan_bwd(ur, f["dt"], f["A"], f["B"], f["C"], cots["dy"].astype(np.float64), dt_bias=f["dt_bias"],
+                          Dskip=f["Dskip"], z=f["z"], h0=f["h0"], dh_final=cots["dh_final"].astype(np.float64))
+    gcr = oracle.conv1d_bwd(f["x"], w64, gsr["dx"], bias=b64, state_in=st)
+    for k, rk in (("dx", "dx"), ("dweight", "dw"), ("dbias", "dbias"), ("dstate_in", "dstate_in")):
+        e = G.rel_max(G.to_np64(gc[k]), gcr[rk])
+        assert e <= 1e-4, (k, e)
+    assert G.rel_max(G.to_np64(gs["dA"]), gsr["dA"]) <= 1e-4
