@@ -142,6 +142,14 @@ def test_conv_scan_full_size_sampled():
     (23, 3, 12, 77, "bf16", 3, False, True),
     (24, 2, 8, 130, "f32", 1, False, False),    # width 1, no activation
     (25, 2, 64, 1000, "bf16", 4, True, True),
+    # rows of a multiple of 8 steps take the 16-byte path: first block (window), interior blocks, last block
+    (26, 3, 10, 256, "f32", 2, True, True),
+    (27, 1, 5, 8, "bf16", 4, True, True),       # one block
+    (28, 2, 7, 24, "f32", 3, True, False),      # first, one interior, last
+    (29, 2, 6, 64, "bf16", 1, False, True),
+    (30, 1, 3, 1, "f32", 4, True, True),        # a single step
+    (31, 2, 3, 2048, "bf16", 4, True, True),    # rows of 128 forward blocks: a wave shares one row
+    (32, 1, 4, 1040, "f32", 3, True, True),     # 16-step forward blocks, ragged 8-step backward tail
 ])
 def test_conv1d_fwd_and_bwd(seed, b, D, L, io, width, state, silu):
     torch = G.torch_dev()
@@ -175,6 +183,26 @@ def test_conv1d_fwd_and_bwd(seed, b, D, L, io, width, state, silu):
     g2 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], du, dc["conv_b"], dc["conv_state"], dso, activation=silu)
     torch.cuda.synchronize()
     assert all(torch.equal(g[k], g2[k]) for k in g)
+
+
+@pytest.mark.parametrize("L", [96, 101])
+def test_conv1d_bf16_outputs(L):
+    # u and dx in bf16 are the round-to-nearest-even of the fp32 results on the same inputs (vector and scalar paths)
+    torch = G.torch_dev()
+    b, D = 2, 11
+    d = I.random_small(41, b, D, L, 16, io="bf16")
+    cv = I.random_small_conv(41, b, D, 16, width=4, with_state=True)
+    dd, dc = G.to_dev(d), G.to_dev(cv)
+    u32 = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], dc["conv_state"], u_dtype=torch.float32)
+    u16 = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], dc["conv_state"], u_dtype=torch.bfloat16)
+    du16 = torch.randn((b, D, L), generator=torch.Generator().manual_seed(41)).to(torch.bfloat16).cuda()
+    g32 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], du16.float(), dc["conv_b"], dc["conv_state"])
+    g16 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], du16, dc["conv_b"], dc["conv_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(u16.view(torch.int16), u32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(g16["dx"].view(torch.int16), g32["dx"].to(torch.bfloat16).view(torch.int16))
+    for k in ("dweight", "dbias", "dstate_in"):
+        assert torch.equal(g16[k], g32[k]), k
 
 
 def test_conv_scan_training_chain():
