@@ -50,13 +50,18 @@ struct Elem<uint16_t> {  // bf16 stored as its bit pattern
 // past num_records returns 0 and a write past it is dropped, so partial tiles need no clamping and cannot fault.
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords: the gfx9-family descriptor format
-constexpr uint32_t kDropOffset = 0x80000000u;  // >= every num_records used below: the access is out of range
+// num_records is an unsigned 32-bit byte count and an access is out of range when offset + size exceeds it.  No
+// descriptor here needs more than 2^31 bytes (16 rows of the longest fp32 sequence: 16 * 2^25 * 4), so ranges are
+// capped at 2^31 and the offset 2^31 is out of range for every descriptor.
+constexpr int64_t kMaxRecords = int64_t(1) << 31;
+constexpr uint32_t kDropOffset = 0x80000000u;
 
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, int64_t elems) {
   int64_t bytes = elems * static_cast<int64_t>(sizeof(T));
-  bytes = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0), static_cast<int>(bytes),
+  bytes = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0),
+                                           static_cast<int>(static_cast<uint32_t>(bytes)),
                                            static_cast<int>(kRsrcWord3));
 }
 
