@@ -102,7 +102,8 @@ KERNEL_SOURCES = (("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")
                   ("decode_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
                   ("bwd_", ("common.hpp", "ssm_scan_bwd.hip")),
                   ("ssd_", ("common.hpp", "ssm_ssd.hip")),
-                  ("complex_", ("common.hpp", "ssm_complex_scan.hip")))
+                  ("complex_", ("common.hpp", "ssm_complex_scan.hip")),
+                  ("conv1d_", ("common.hpp", "scan_fwd.hpp", "ssm_conv_scan.hip")))
 
 
 def ssd_decode_algorithmic_bytes(b, H, P, G, N, io_bytes=2, gate=True):
@@ -319,7 +320,8 @@ def main():
             out["conv_scan"]["conv1d_" + name] = {
                 "ms": ctimes[name], "algorithmic_bytes": cby[name],
                 "roofline": {"bound": "hbm", "achieved": gbs_, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs_ / HBM_PEAK_GBS}}
+                             "frac": gbs_ / HBM_PEAK_GBS,
+                             "traffic": measured_traffic("conv1d_%s_kernel<bf16,bf16,4> mamba2.8b-layer" % name)}}
         del uu, gdx
 
     # ---- complex diagonal A (S4D-Lin) on the same shape: complex B, C and state
@@ -452,7 +454,8 @@ def main():
                              "roofline": {"bound": "hbm", "achieved": sdby / (sdms * 1e-3) / 1e9,
                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                           "frac": sdby / (sdms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                          "algorithmic_bytes": sdby}}
+                                          "algorithmic_bytes": sdby,
+                                          "traffic": measured_traffic("ssd_decode_kernel mamba2-decode-b256")}}
         del sstate, sin
 
     # ---- backward over the same workload: bf16 dy in, bf16 dx / ddt / dz out, fp32 parameter gradients
