@@ -9,7 +9,7 @@ models, million-length sequences as in the DNA and audio experiments (sections 4
 decode (section 4.5).  Initialisations follow section 3.6: A from S4D-Real, A_n = -(n+1), and the Delta bias drawn as
 softplus^-1 of a value log-uniform in a range around [0.001, 0.1].
 
-Recipe (also written out in the design doc):
+Recipe:
   * every tensor k of workload `cfg` at decode step `step` is drawn in flattened chunks of 2**24 elements, chunk i
     from numpy's default_rng(SeedSequence(57, spawn_key=(cfg, step, k, i)));
   * tensor order k: 0 x, 1 Delta*, 2 bias, 3 A-jitter, 4 B, 5 C, 6 Dskip, 7 z, 8 h0/state, 9 dy, 10 dh_final
