@@ -124,6 +124,16 @@ def src_hash(kernel_key):
     return h.hexdigest()[:16]
 
 
+def ssd_traffic(nseg):
+    """HBM bytes of one ssm_ssd_fwd call on the 2.7B layer: the full pass, plus the zero-start pass when the
+    sequence is split into L-segments; None unless every record involved is current."""
+    full = measured_traffic("ssd_fwd_kernel mamba2-2.7b-layer")
+    if nseg <= 1 or full is None:
+        return full
+    zero = measured_traffic("ssd_fwd_kernel zero-start mamba2-2.7b-layer")
+    return None if zero is None else full + zero
+
+
 def measured_traffic(kernel_key):
     """HBM bytes per launch (read + written) from the committed rocprofv3 counter record, if it was taken on the
     current kernel source; None otherwise."""
@@ -399,9 +409,9 @@ def main():
                       "ms_per_step": sms, "elements_per_s": selem / (sms * 1e-3),
                       "ratio_to_s6_scan_same_elements": sms / ms if selem == elems else None,
                       "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": sgbs / HBM_PEAK_GBS, "traffic": measured_traffic("ssd_fwd_kernel "
-                                                                                            "mamba2-2.7b-layer"),
-                                   "kernel": "ssd_fwd_kernel<128,bf16,euler,gate,dskip>",
+                                   "frac": sgbs / HBM_PEAK_GBS, "traffic": ssd_traffic(snseg),
+                                   "kernel": "ssd_fwd_kernel<128,bf16,euler,gate,dskip> (+ the zero-start pass "
+                                             "over all but the last L-segment)",
                                    "algorithmic_bytes": sby},
                       "mfma": {"algorithmic_flops": sfl, "achieved_TFLOPs": stf, "peak_bf16_TFLOPs": 2500.0,
                                "frac": stf / 2500.0}}

@@ -648,7 +648,17 @@ SsdPlan ssd_plan(const ssm_ssd_params* p) {
   SsdPlan pl{};
   pl.nchunks = static_cast<int>((p->seqlen + kQ - 1) / kQ);
   const int64_t nbh = p->batch * p->nheads;
-  int64_t want = p->segments > 0 ? p->segments : (nbh >= 256 ? 1 : (1280 + nbh - 1) / nbh);
+  // Segments trade the zero-start pass (the state update over all but the last segment) for balance across the
+  // 256 CUs (at most two workgroups each) and shorter chunk chains.  Measured on 80 heads x 64, N = 128, L = 4096:
+  // 80 pairs: 6 segments best (89 us; 16: 159), 160: 3 (154; 1: 240), 320: 3 (301; 1: 338), 640: 1 (545; 2: 564).
+  // So about 480 work items below 256 pairs, about 960 up to 512, one segment from there on.
+  int64_t want;
+  if (p->segments > 0)
+    want = p->segments;
+  else if (nbh >= 512)
+    want = 1;
+  else
+    want = ((nbh >= 256 ? 960 : 480) + nbh / 2) / nbh;
   want = want < 1 ? 1 : (want > pl.nchunks ? pl.nchunks : want);
   pl.cps = static_cast<int>((pl.nchunks + want - 1) / want);
   pl.nseg = (pl.nchunks + pl.cps - 1) / pl.cps;
