@@ -157,3 +157,36 @@ def test_bwd_full_size_sampled(cfg, ndim):
         got[k] = np.take(a, chans, axis=axis)
     errs = {k: G.rel_max(got[k], ref[rk]) for k, rk in KEYS.items()}
     assert all(e <= TOL_BWD for e in errs.values()), errs
+
+
+def test_bwd_million_length_sampled():
+    """The million-step layer (1 x 512 x 2^20, 16,384 chunks) at full size, with dy and dh_final non-zero only on
+    three channels (seeded normals; the backward is linear in them): those channels' gradients and the full dB / dC
+    against the oracle run on the three channels, every other channel's gradients exactly zero."""
+    torch = G.torch_dev()
+    w = I.WORKLOADS[3]
+    print("million-length backward: generating inputs", flush=True)
+    d = I.scan_inputs(w, with_h0=True)
+    chans = np.array([0, 301, w.dim - 1])
+    r = np.random.default_rng(33)
+    dy = np.zeros((w.batch, w.dim, w.seqlen), np.float32)
+    dy[:, chans] = r.standard_normal((w.batch, len(chans), w.seqlen), dtype=np.float32)
+    dhf = np.zeros((w.batch, w.dim, w.dstate), np.float32)
+    dhf[:, chans] = r.standard_normal((w.batch, len(chans), w.dstate), dtype=np.float32)
+    print("million-length backward: GPU", flush=True)
+    g = run_bwd(G.to_dev(d), G.to_dev({"dy": dy, "dh_final": dhf}))
+    sub = {k: (None if v is None else (v[:, chans] if k in ("x", "dt", "z", "h0") else
+                                       (v[chans] if k in ("A", "dt_bias", "Dskip") else v)))
+           for k, v in d.items()}
+    print("million-length backward: oracle on %d channels" % len(chans), flush=True)
+    ref = oracle_bwd(sub, {"dy": dy[:, chans], "dh_final": dhf[:, chans]})
+    errs = {}
+    for k, rk in KEYS.items():
+        a = G.to_np64(g[k])
+        if k not in ("dB", "dC"):
+            axis = 1 if k in ("dx", "ddt", "dz", "dh0") else 0
+            assert not np.any(np.delete(a, chans, axis=axis)), (k, "non-zero gradient outside the sampled channels")
+            a = np.take(a, chans, axis=axis)
+        errs[k] = G.rel_max(a, ref[rk])
+    print("million-length backward errors:", {k: "%.1e" % e for k, e in errs.items()}, flush=True)
+    assert all(e <= TOL_BWD for e in errs.values()), errs
