@@ -8,8 +8,8 @@
 //
 // Same work split as the real kernel: one lane per (channel, n), a 16-lane row per channel, 16 channels per
 // workgroup, Delta and Delta x broadcast from the step's owner lane by DPP.  Per step a lane needs |Abar| = exp2, the
-// phase's cos / sin (the device library's accurate sincosf: the hardware sine's per-step error would accumulate over
-// the decay memory) and a complex multiply-add.  B and C of a 16-step block are staged in LDS as fp32 (one complex
+// phase's cos / sin to about an ulp (`sincos_cw`: the hardware sine's per-step error would accumulate over the decay
+// memory) and a complex multiply-add.  B and C of a 16-step block are staged in LDS as fp32 (one complex
 // value of each per thread), and each lane writes Re(C_n h_n) of every step to LDS so that the step's owner only adds
 // 16 values.  No L-segments: channels give the parallelism (the
 // workloads that use complex A are channel-rich).
@@ -37,6 +37,41 @@ struct CScanArgs {
   int64_t batch, dim, L;
   int N, softplus;
 };
+
+// sin and cos of x by Cody and Waite's reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
+// Functions", 1980): x = k pi/2 + r with pi/2 = P1 + P2 + P3 (the float nearest pi/2 and two float remainders, 72 bits
+// together), each step one fused multiply-add, so r is within about an ulp for |x| < 2^22; then Taylor polynomials
+// on |r| <= pi/4 (sin to r^9, cos to r^10: truncation below 2^-27) and the quadrant's swap and signs.  No branch:
+// the general library routine carries a large-argument path that costs even when it is not taken (6 % of the scan).
+// The phase Delta Im(A) is an fp32 product, meaningless beyond 2^22 anyway; there r is clamped so the results stay
+// bounded.
+__device__ __forceinline__ void sincos_cw(float x, float* sp, float* cp) {
+  constexpr float kTwoOverPi = 0.636619772367581343f;
+  constexpr float kP1 = 1.57079637050628662109375f;   // float(pi/2)
+  constexpr float kP2 = -4.37113900018624283e-8f;      // float(pi/2 - P1)
+  constexpr float kP3 = -1.7151245100058819e-15f;      // float(pi/2 - P1 - P2)
+  const float k = __builtin_rintf(x * kTwoOverPi);
+  float r = fmaf(-k, kP1, x);
+  r = fmaf(-k, kP2, r);
+  r = fmaf(-k, kP3, r);
+  r = fminf(fmaxf(r, -2.0f), 2.0f);
+  const float r2 = r * r;
+  // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9!),  cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
+  float ps = fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+  ps = fmaf(r2, ps, 1.0f / 120.0f);
+  ps = fmaf(r2, ps, -1.0f / 6.0f);
+  const float sr = fmaf(r * r2, ps, r);
+  float pc = fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+  pc = fmaf(r2, pc, -1.0f / 720.0f);
+  pc = fmaf(r2, pc, 1.0f / 24.0f);
+  pc = fmaf(r2, pc, -0.5f);
+  const float cr = fmaf(r2, pc, 1.0f);
+  // quadrant q = k mod 4: (sin, cos) = (S, C), (C, -S), (-S, -C), (-C, S)
+  const int q = static_cast<int>(k) & 3;
+  const float s0 = (q & 1) ? cr : sr, c0 = (q & 1) ? sr : cr;
+  *sp = (q & 2) ? -s0 : s0;
+  *cp = ((q + 1) & 2) ? -c0 : c0;
+}
 
 // complex value (re, im) of a [..][2] io-dtype array at complex index i
 template <typename T>
@@ -126,7 +161,7 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
       const float dk = row_bcast<K>(delta);
       const float mag = hw_exp2(dk * Ar2);
       float s, c;
-      sincosf(dk * Aim, &s, &c);  // accurate: the phase error would otherwise accumulate over the decay memory
+      sincos_cw(dk * Aim, &s, &c);  // accurate to about an ulp: phase errors accumulate over the decay memory
       const float abr = mag * c, abi = mag * s;
       const float2 bq = sB[n][K];
       float bbr, bbi;
@@ -203,7 +238,7 @@ __global__ __launch_bounds__(256) void complex_decode_kernel(CDecodeArgs p) {
   const float delta = p.softplus ? softplus(uv) : uv;
   const float mag = hw_exp2(delta * Are * kLog2e);
   float s, c;
-  sincosf(delta * Aim, &s, &c);
+  sincos_cw(delta * Aim, &s, &c);
   float bbr, bbi;
   if constexpr (ZOH) {
     const float den = Are * Are + Aim * Aim;

@@ -104,3 +104,31 @@ def test_complex_full_size_sampled():
         yr, _ = ref(sub)
         exp.append(yr[0, 0])
     assert G.rel_max(got, np.stack(exp)) <= G.TOL_BF16
+
+
+def test_complex_decode_large_exact_phases():
+    """Rotation by large phases.  With Re(A) = 0 and x = 0 a step is the pure rotation h <- exp(i Delta Im(A)) h;
+    Delta (softplus off) and Im(A) have few significant bits, so the fp32 phase is exact (up to 1.3e5 rad) and the
+    result differs from the fp64 oracle only by the sine and cosine's error (about an ulp after the reduction) and
+    the complex multiply's rounding: 1e-6 of rms would catch a sine or cosine off by a few 1e-7."""
+    torch = G.torch_dev()
+    b, D, N = 2, 8, 16
+    r = np.random.default_rng(77)
+    A = np.zeros((D, N, 2), np.float32)
+    A[..., 1] = (np.arange(N) + 1)[None, :] * np.array([0.75, 13.5, 96.25, 613.25, 1024.5, 2049.75, 3000.5, 4096.25],
+                                                       np.float32)[:, None]
+    dt = r.choice(np.array([0.25, 0.5, 1.0, 1.5, 2.0], np.float32), (b, D)).astype(np.float32)
+    x = np.zeros((b, D), np.float32)
+    Bc = r.standard_normal((b, N, 2), dtype=np.float32)
+    Cc = r.standard_normal((b, N, 2), dtype=np.float32)
+    h0 = r.standard_normal((b, D, N, 2), dtype=np.float32)
+    assert np.all(np.abs(dt[:, :, None].astype(np.float64) * A[None, :, :, 1]) < 1.4e5)
+    t = lambda a: torch.from_numpy(a).cuda()
+    state = t(h0.copy())
+    y = ssm.complex_state_update(state, t(x), t(dt), t(A), t(Bc), t(Cc), softplus=False, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, sr = oracle.complex_state_update(h0.astype(np.float64), x, dt, A, Bc, Cc, softplus=False)
+    assert G.rel_max(G.to_np64(y), yr) <= 1e-6
+    st = G.to_np64(state)
+    sref = np.stack([sr.real, sr.imag], axis=-1)
+    assert G.rel_max(st, sref) <= 1e-6
