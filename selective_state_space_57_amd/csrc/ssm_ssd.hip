@@ -637,9 +637,7 @@ ssm_status dispatch_fwd(const ssm_ssd_params* p, SsdArgs a, bool gate, bool dski
              : launch_fwd<N, uint16_t, false, false>(a, gate, dskip, st);
 }
 
-// Segments along L: when the (batch, head) pairs alone leave CUs idle (fewer than 256 of them), split L so that
-// there are about 1280 work items, at least one 64-step chunk each.  With 256 pairs or more one segment is kept:
-// the zero-start pass then costs about what the better balance gains.
+// Segments along L (at least one 64-step chunk each); the count is chosen in ssd_plan.
 struct SsdPlan {
   int nchunks, nseg, cps;
   size_t state_bytes, sum_bytes;
