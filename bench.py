@@ -266,6 +266,22 @@ def main():
         "host_wall_ms_timed_region": wall_ms,
     }
 
+    # ---- context: what a plain device-to-device copy reaches here (1 GiB, read + written, timed after the scan)
+    cp_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * cp_src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    out["hbm"]["copy_ceiling_GBps"] = copy_gbs
+    out["hbm"]["frac_of_copy_ceiling"] = gbs / copy_gbs
+    del cp_src, cp_dst
+
     # ---- the same forward with the block's causal convolution (width 4) + SiLU fused in front of the scan
     if not args.no_conv:
         from selective_state_space_57_amd import _abi
