@@ -180,3 +180,16 @@ def test_ssd_full_size_sampled_heads():
         print("full size head %d: y err %.2e, h err %.2e" % (h, ey, eh), flush=True)
         assert ey <= TOL_SSD and eh <= TOL_SSD, (h, ey, eh)
     assert bool(torch.isfinite(y).all())
+
+
+@pytest.mark.parametrize("disc", [0, 1])
+def test_ssd_zero_A_heads(disc):
+    # heads with A = 0 never decay (ZOH's coefficient is then Delta itself); mixed with decaying heads, ragged length
+    d = I.random_small_ssd(15 + disc, 2, 150, 4, 64, 2, 128, h0=True)
+    d["A"] = d["A"].copy()
+    d["A"][[0, 3]] = 0.0
+    dd = G.to_dev(d)
+    y, hf = run(dd, disc=disc)
+    yr, hr = ref(d, disc=disc)
+    assert G.rel_max(G.to_np64(y), yr) <= TOL_SSD
+    assert G.rel_max(G.to_np64(hf), hr) <= TOL_SSD
