@@ -176,6 +176,13 @@ MUTANTS = [
     ("ssd_decode_bias", r"const double u = dt\[b \* H \+ h\] \+ \(dt_bias \? dt_bias\[h\] : 0\.0\);",
      "const double u = dt[b * H + h];"),
     ("ssd_x_head0", r"const double xv = x\[row \* P \+ p\];", "const double xv = x[(row - h) * P + p];"),
+    # decode-only code paths of the complex and SSD layers
+    ("complex_decode_dskip_dropped", r"if \(Dskip\) yv \+= Dskip\[d\] \* x\[bd\];", "if (Dskip) yv += 0.0;"),
+    ("complex_decode_gate_dropped", r"if \(z\) yv \*= z\[bd\] / \(1\.0 \+ exp\(-z\[bd\]\)\);", "if (z) yv *= 1.0;"),
+    ("ssd_decode_gate_sign", r"if \(z\) acc \*= z\[i\] / \(1\.0 \+ exp\(-z\[i\]\)\);",
+     "if (z) acc *= z[i] / (1.0 + exp(z[i]));"),
+    ("ssd_decode_zoh_no_div", r"expm1\(delta \* Ah\) / Ah\);(\s+const double\* Bt = B \+ \(b \* G)",
+     r"expm1(delta * Ah));\1"),
 ]
 
 
