@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(ConvArgs a, int vec, St
       for (int k = 0; k < K; ++k) pre = fmaf(w[k], xv[4 + j - S + k], pre);
       o[j] = a.silu ? silu(pre) : pre;
     }
-    if (vec) {   // rows of a multiple of 8: every block is whole
+    if (vec) {   // rows of a multiple of 16 steps: every block is whole
       Vec<TO>::st8(ur + t0, o);
       Vec<TO>::st8(ur + t0 + 8, o + 8);
     } else {
