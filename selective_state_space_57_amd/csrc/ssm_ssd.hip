@@ -43,6 +43,8 @@ constexpr int kQ = 64;         // chunk length (steps)
 constexpr int kP = 64;         // head width (columns per head)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kTiles = 10;     // lower-triangular 16x16 tiles of a 64x64 chunk
+constexpr int kMSlots = 6;     // pairs of them along s: (tb, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__host__ __device__ constexpr int mslot(int tb, int kk) { return tb + (tb == 3 ? 1 : 0) + kk; }
 
 // LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), stored with the 16-byte
 // units of each row permuted (unit u of row r sits at u ^ f(r)) so that both the row-wise operand reads (16 rows, one
@@ -161,18 +163,40 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
   return v + (row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f) + (row >= 3 ? r2 : 0.0f);
 }
 
+// Global -> LDS copy of one chunk's rows into a permuted array: copy i of a lane (i < kInstr) moves 16-byte unit
+// (P % U) ^ f(r) of row r = P / U, P = 64 (wave + 4 i) + lane, into LDS slot 512 (wave + 4 i) + 8 lane.  A lane's
+// copies lie kStep rows apart and the permutation sees only the low four bits of a row, so the lane keeps one byte
+// offset per residue class of its rows modulo 16 (kBases of them, computed once) and each chunk adds its first row
+// as a workgroup-uniform offset.  Rows at or past the sequence end lie outside the batch element's buffer range and
+// read as zeros.
+template <int U>
+struct Stage {
+  static constexpr int kInstr = kQ * U / 256;
+  static constexpr int kStep = 256 / U;
+  static constexpr int kBases = kStep >= 16 ? 1 : 16 / kStep;
+  static_assert(kStep % 16 == 0 || 16 % kStep == 0, "row step must divide or be a multiple of 16");
+  uint32_t base[kBases];
+};
 template <int U, int KIND>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t rsrc, int wave, int lane, int t0,
-                                           int L, int row_elems, int col0) {
-  constexpr int kInstr = kQ * U / 64;
+__device__ __forceinline__ Stage<U> stage_init(int wave, int lane, uint32_t row_elems, uint32_t col0) {
+  Stage<U> st;
 #pragma unroll
-  for (int i = 0; i < kInstr / 4; ++i) {
-    const int k = wave + 4 * i;
-    const int P = 64 * k + lane;
+  for (int j = 0; j < Stage<U>::kBases; ++j) {
+    const int P = 64 * (wave + 4 * j) + lane;
     const int r = P / U, u = (P % U) ^ (swz<KIND>(r) & (U - 1));
-    const int t = t0 + r;
-    const uint32_t o = t < L ? static_cast<uint32_t>((int64_t(t) * row_elems + col0 + 8 * u) * 2) : kDropOffset;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 512 * k), 16, static_cast<int>(o), 0, 0, 0);
+    st.base[j] = (static_cast<uint32_t>(r) * row_elems + col0 + 8u * static_cast<uint32_t>(u)) * 2u;
+  }
+  return st;
+}
+template <int U>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t rsrc, const Stage<U>& st, int wave,
+                                           uint32_t row0_bytes, uint32_t row_bytes) {
+  using S = Stage<U>;
+#pragma unroll
+  for (int i = 0; i < S::kInstr; ++i) {
+    const uint32_t o = st.base[i % S::kBases] + row0_bytes + static_cast<uint32_t>(i / S::kBases * S::kBases * S::kStep) * row_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 512 * (wave + 4 * i)), 16, static_cast<int>(o), 0,
+                                             0, 0);
   }
 }
 
@@ -200,7 +224,9 @@ ssd_fwd_kernel(SsdArgs a) {
   __shared__ alignas(16) uint16_t sB0[kQ * N], sB1[kQ * N];    // B[s][n], double-buffered
   __shared__ alignas(16) uint16_t sX0[kQ * kP], sX1[kQ * kP];  // x[s][p], double-buffered
   __shared__ alignas(16) uint16_t sC[kQ * N];                  // C[t][n]
-  __shared__ u2 sM[kTiles][2][64];   // M tiles in accumulator layout: [tile][hi, lo][lane] -> 4 bf16
+  // M tiles in accumulator layout, paired as operands of the x M product: slot mslot(tb, kk) holds per lane the 4 bf16
+  // of tile (tb, 2 kk) and then those of tile (tb, 2 kk + 1) (zeros where that tile lies above the diagonal), [hi, lo]
+  __shared__ u4 sM[kMSlots][2][64];
   __shared__ Scal sSc[2];   // per-step scalars of a chunk, computed by wave 0; alternate chunks use alternate copies
 
   const int tid = threadIdx.x;
@@ -262,18 +288,38 @@ ssd_fwd_kernel(SsdArgs a) {
   }
   float dsum = 0.0f;   // sum of Delta over this segment (zero-start pass)
 
+  // Byte offsets are 32-bit (the host keeps every row up to two chunks past the end below 2^32 bytes); rows at or
+  // past the end lie outside the batch element's buffer range, so their loads read zeros and their stores are dropped.
+  const uint32_t dt_row = static_cast<uint32_t>(a.H) * 2u;   // bytes per step of dt
+  const uint32_t dt_base = static_cast<uint32_t>(lane) * dt_row + static_cast<uint32_t>(h) * 2u;
   auto load_dt = [&](int ck) -> uint32_t {
-    const int t = ck * kQ + lane;
-    const uint32_t o = t < L ? static_cast<uint32_t>((int64_t(t) * a.H + h) * 2) : kDropOffset;
+    const uint32_t o = dt_base + static_cast<uint32_t>(ck * kQ) * dt_row;
     return static_cast<uint32_t>(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, static_cast<int>(o),
                                                                                             0, 0)));
   };
-  const int grow = a.G * N, gcol = g * N;          // B / C: row stride and column offset of this group
-  const int xrow_e = a.H * kP, xcol = h * kP;      // x: row stride and column offset of this head
-  stage_rows<U, kSwzB>(sB0, rB, wave, lane, c0 * kQ, L, grow, gcol);
-  if constexpr (!SEGST) stage_rows<U, kSwzC>(sC, rC, wave, lane, c0 * kQ, L, grow, gcol);
-  stage_rows<8, kSwzX>(sX0, rx, wave, lane, c0 * kQ, L, xrow_e, xcol);
+  const uint32_t grow = static_cast<uint32_t>(a.G * N), gcol = static_cast<uint32_t>(g * N);   // B / C row, group
+  const uint32_t xrow_e = static_cast<uint32_t>(a.H * kP), xcol = static_cast<uint32_t>(h * kP);   // x row, head
+  const uint32_t bc_row = grow * 2u, x_row = xrow_e * 2u;   // bytes per step
+  const Stage<U> stB = stage_init<U, kSwzB>(wave, lane, grow, gcol);
+  const Stage<U> stC = stage_init<U, kSwzC>(wave, lane, grow, gcol);
+  const Stage<8> stX = stage_init<8, kSwzX>(wave, lane, xrow_e, xcol);
+  // z and y at this lane's output positions t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
+  const uint32_t zy_elem = static_cast<uint32_t>(l16) * xrow_e + xcol + static_cast<uint32_t>(16 * wave + 4 * g4);
+  const uint32_t z_base = zy_elem * 2u, y_base = zy_elem * static_cast<uint32_t>(sizeof(TY));
+  const uint32_t y_row = xrow_e * static_cast<uint32_t>(sizeof(TY));
+  stage_rows<U>(sB0, rB, stB, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
+  if constexpr (!SEGST) stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
+  stage_rows<8>(sX0, rx, stX, wave, static_cast<uint32_t>(c0 * kQ) * x_row, x_row);
   uint32_t dtw = wave == 0 ? load_dt(c0) : 0u;
+  if constexpr (!SEGST) {
+    if (wave == 0) {   // the halves of the pair slots whose second tile lies above the diagonal stay zero
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        reinterpret_cast<u2*>(&sM[mslot(0, 0)][e][lane])[1] = u2{0u, 0u};
+        reinterpret_cast<u2*>(&sM[mslot(2, 1)][e][lane])[1] = u2{0u, 0u};
+      }
+    }
+  }
 
   // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
   auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn, Scal& sc)
@@ -317,15 +363,13 @@ ssd_fwd_kernel(SsdArgs a) {
         zo[tb] = u2{0u, 0u};
         continue;
       }
-      const int t = t0 + 16 * tb + l16;
-      const uint32_t o = t < L ? static_cast<uint32_t>(((int64_t(t) * a.H + h) * kP + 16 * wave + 4 * g4) * 2)
-                               : kDropOffset;
+      const uint32_t o = z_base + static_cast<uint32_t>(t0 + 16 * tb) * x_row;
       zo[tb] = GATE ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<int>(o), 0, 0))
                     : u2{0u, 0u};
     }
     // the next chunk's copies (past the last chunk they read zeros into a buffer nobody reads)
-    stage_rows<U, kSwzB>(Bn, rB, wave, lane, t0 + kQ, L, grow, gcol);
-    stage_rows<8, kSwzX>(Xn, rx, wave, lane, t0 + kQ, L, xrow_e, xcol);
+    stage_rows<U>(Bn, rB, stB, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
+    stage_rows<8>(Xn, rx, stX, wave, static_cast<uint32_t>(t0 + kQ) * x_row, x_row);
     if (wave == 0) dtw = load_dt(ck + 1);
     const float* sac = sc.ac;
 
@@ -353,8 +397,8 @@ ssd_fwd_kernel(SsdArgs a) {
       }
       u2 hi, lo;
       split4(m[0], m[1], m[2], m[3], hi, lo);
-      sM[ti][0][lane] = hi;
-      sM[ti][1][lane] = lo;
+      reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][0][lane])[sb & 1] = hi;
+      reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][1][lane])[sb & 1] = lo;
     }
 
     // ---- inter-chunk part: Y^T[p][t] = sum_n S_prev[p][n] C[t][n], scaled by E_t = exp2(ac_t)
@@ -421,7 +465,7 @@ ssd_fwd_kernel(SsdArgs a) {
     }
     if constexpr (SEGST) return;            // the zero-start pass only carries the state
     lds_barrier();                          // M tiles are in LDS; every wave is done with C
-    stage_rows<U, kSwzC>(sC, rC, wave, lane, t0 + kQ, L, grow, gcol);
+    stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
 
     // ---- intra-chunk part: Y^T[p][t] += sum_{s <= t} x^T[p][s] M[t][s]
     {
@@ -436,15 +480,8 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           if (32 * kk > 16 * tb + 15) continue;   // the whole k-step lies above the diagonal
-          const int sb0 = 2 * kk, sb1 = 2 * kk + 1;
-          const int t0i = tb * (tb + 1) / 2;
-          const u2 zero = {0u, 0u};
-          const u2 h0v = sM[t0i + sb0][0][lane];
-          const u2 l0v = sM[t0i + sb0][1][lane];
-          const u2 h1v = sb1 <= tb ? sM[t0i + sb1][0][lane] : zero;
-          const u2 l1v = sb1 <= tb ? sM[t0i + sb1][1][lane] : zero;
-          acc[tb] = mfma(ax, cat(h0v, h1v), acc[tb]);
-          acc[tb] = mfma(ax, cat(l0v, l1v), acc[tb]);
+          acc[tb] = mfma(ax, sM[mslot(tb, kk)][0][lane], acc[tb]);
+          acc[tb] = mfma(ax, sM[mslot(tb, kk)][1][lane], acc[tb]);
         }
       }
     }
@@ -453,7 +490,6 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int tl = 16 * tb + l16;
-      const int t = t0 + tl;
       const u2 xw2 = DSKIP ? lds8(at(Xc, soff<8, kSwzX>(tl, 2 * wave + (g4 >> 1)) + (g4 & 1) * 8)) : u2{0u, 0u};
       float v[4];
 #pragma unroll
@@ -466,9 +502,7 @@ ssd_fwd_kernel(SsdArgs a) {
         if (GATE) yv *= silu(zv);
         v[c] = yv;
       }
-      const uint32_t o = t < L ? static_cast<uint32_t>(((int64_t(t) * a.H + h) * kP + 16 * wave + 4 * g4) *
-                                                       static_cast<int64_t>(sizeof(TY)))
-                               : kDropOffset;
+      const uint32_t o = y_base + static_cast<uint32_t>(t0 + 16 * tb) * y_row;
       if constexpr (sizeof(TY) == 4) {
         const u4 ov = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
         __builtin_amdgcn_raw_buffer_store_b128(ov, ry, static_cast<int>(o), 0, 0);
@@ -595,7 +629,11 @@ ssm_status check_ssd(const ssm_ssd_params* p, bool need_seqlen) {
   if (p->segments < 0) return fail(SSM_ERR_UNSUPPORTED, "segments must be >= 0 (got %d)", p->segments);
   const int64_t L = need_seqlen ? p->seqlen : 1;
   // buffer offsets are 32-bit: one batch element of x / y (fp32 y: 4 bytes) and of B / C must stay below 2^31 bytes
-  if (L * p->nheads * kP * 4 >= (int64_t(1) << 31) || L * p->ngroups * p->dstate * 2 >= (int64_t(1) << 31))
+  // (the largest buffer range), and the offsets the forward kernel forms for rows up to two chunks past the end
+  // (the last chunk's padding and the prefetch after it) below 2^32
+  const int64_t Lp = L + 2 * kQ;
+  if (L * p->nheads * kP * 4 >= (int64_t(1) << 31) || L * p->ngroups * p->dstate * 2 >= (int64_t(1) << 31) ||
+      Lp * p->nheads * kP * 4 >= (int64_t(1) << 32) || Lp * p->ngroups * p->dstate * 2 >= (int64_t(1) << 32))
     return fail(SSM_ERR_SHAPE, "seqlen * nheads * headdim too large for one batch element");
   if (p->batch * p->nheads >= (int64_t(1) << 31)) return fail(SSM_ERR_SHAPE, "batch * nheads too large");
   return SSM_OK;
