@@ -38,7 +38,12 @@ using namespace ssm57;
 constexpr int kBT = 64;              // steps per chunk
 constexpr int kBlk = 16;             // steps per block (= lanes per row)
 constexpr int kNB = kBT / kBlk;      // blocks per chunk
-constexpr int kSlots = kNB + 1;      // per (channel, chunk): local states after blocks 0..kNB-2, end state, lambda
+// Per (channel, chunk) record of side values, 6 slots of 16 floats (384 bytes, a multiple of the 128-byte line): slot 0
+// the chunk's end state from a zero start (the carry turns it into the entering state), slot 1 lambda (turned into
+// the entering adjoint), slots 2..4 the local states after blocks 0..kNB-2, slot 5 padding.  The carry touches only
+// slots 0 and 1, which share one line.
+constexpr int kRec = 6;
+constexpr int kSlotIn = 0, kSlotLam = 1, kSlotLoc = 2;
 constexpr int kNP = 16;              // state axis padded to 16 in workspace arrays
 constexpr int kSStride = kBT + 4;    // sB / sC row stride (floats): conflict-free b128 reads along t
 constexpr int kTStride = kNP + 4;    // sBt / sCt ([t][n] copies) step stride: conflict-free b128 reads along n
@@ -68,7 +73,7 @@ struct BwdArgs {
   float* dD;
   float* dbias;
   float* dh0;
-  float* side;    // [batch*dim][nck][kSlots][16]
+  float* side;    // [batch*dim][nck][kRec][16]
   float* cum;     // [batch*dim][nck][kNB]: sum of Delta from the chunk start through block i
   float* partBC;  // [G][batch][2][16][Lpad]: per-workgroup dB (0) / dC (1)
   float* partA;   // [batch*nck][dim][16]
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     const float Ap = An * kLog2e;
     const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
     const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
-    float* const sp = p.side + (bd * p.nck + k) * (kSlots * kNP) + n;
+    float* const sp = p.side + (bd * p.nck + k) * (kRec * kNP) + n;
     float* const cp = p.cum + (bd * p.nck + k) * kNB;
     const int boff = opaque(n * kSStride);
     float h = 0.0f, E = 1.0f, lam = 0.0f, cum = 0.0f;
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
       s += __shfl_xor(s, 1, 16);
       cum += s;
       if (chv) {
-        sp[I * kNP] = h;
+        sp[(I == kNB - 1 ? kSlotIn : kSlotLoc + I) * kNP] = h;
         if (n == 0) cp[I] = cum;
       }
       pin(h);
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
       pin(lam);
       pin(cum);
     });
-    if (chv) sp[kNB * kNP] = lam;
+    if (chv) sp[kSlotLam * kNP] = lam;
   }
 }
 
@@ -322,21 +327,21 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
   if (bd >= p.batch * p.dim || n >= p.N) return;
   const int64_t d = bd % p.dim;
   const float Ap = p.A[d * p.N + n] * kLog2e;
-  float* const sp = p.side + bd * p.nck * (kSlots * kNP) + n;
+  float* const sp = p.side + bd * p.nck * (kRec * kNP) + n;
   const float* const cp = p.cum + bd * p.nck * kNB + (kNB - 1);
-  auto slot = [&](int k, int j) { return sp + static_cast<int64_t>(k) * (kSlots * kNP) + j * kNP; };
+  auto slot = [&](int k, int j) { return sp + static_cast<int64_t>(k) * (kRec * kNP) + j * kNP; };
   float hs = p.h0 ? p.h0[bd * p.N + n] : 0.0f;
   for (int k0 = 0; k0 < p.nck; k0 += U) {
     float e[U], P[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = k0 + u < p.nck;
-      e[u] = ok ? *slot(k0 + u, kNB - 1) : 0.0f;
+      e[u] = ok ? *slot(k0 + u, kSlotIn) : 0.0f;
       P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k0 + u) * kNB] * Ap) : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k0 + u < p.nck) *slot(k0 + u, kNB - 1) = hs;
+      if (k0 + u < p.nck) *slot(k0 + u, kSlotIn) = hs;
       hs = fmaf(P[u], hs, e[u]);
     }
   }
@@ -346,12 +351,12 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = k1 - u >= 0;
-      l[u] = ok ? *slot(k1 - u, kNB) : 0.0f;
+      l[u] = ok ? *slot(k1 - u, kSlotLam) : 0.0f;
       P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k1 - u) * kNB] * Ap) : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k1 - u >= 0) *slot(k1 - u, kNB) = rho;
+      if (k1 - u >= 0) *slot(k1 - u, kSlotLam) = rho;
       rho = fmaf(P[u], rho, l[u]);
     }
   }
@@ -404,14 +409,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int64_t d = chan(q);
     const bool ok = q < p.Q && d < p.dim;
     const int64_t bd = b * p.dim + (ok ? d : 0);
-    const float* sp = p.side + (bd * p.nck + k) * (kSlots * kNP) + n;
+    const float* sp = p.side + (bd * p.nck + k) * (kRec * kNP) + n;
     const float* cp = p.cum + (bd * p.nck + k) * kNB;
-    s.hin = (ok && nv) ? sp[(kNB - 1) * kNP] : 0.0f;
-    s.rho = (ok && nv) ? sp[kNB * kNP] : 0.0f;
+    s.hin = (ok && nv) ? sp[kSlotIn * kNP] : 0.0f;
+    s.rho = (ok && nv) ? sp[kSlotLam * kNP] : 0.0f;
     s.hl[0] = s.cm[0] = 0.0f;
 #pragma unroll
     for (int i = 1; i < kNB; ++i) {
-      s.hl[i] = (ok && nv) ? sp[(i - 1) * kNP] : 0.0f;
+      s.hl[i] = (ok && nv) ? sp[(kSlotLoc + i - 1) * kNP] : 0.0f;
       s.cm[i] = ok ? cp[i - 1] : 0.0f;
     }
     return s;
@@ -710,7 +715,7 @@ BwdPlan make_bwd_plan(const ssm_scan_params* p) {
   auto up = [](size_t v) { return (v + 63) & ~static_cast<size_t>(63); };
   size_t off = 0;
   pl.off_side = off;
-  off += up(bd * nck * kSlots * kNP);
+  off += up(bd * nck * kRec * kNP);
   pl.off_cum = off;
   off += up(bd * nck * kNB);
   pl.off_bc = off;
