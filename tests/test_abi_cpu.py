@@ -177,6 +177,9 @@ def call_ssd(p, ws=0, ws_bytes=0, **ptrs):
     (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2), (dict(headdim=32), 4),
     (dict(dstate=16), 4), (dict(dstate=96), 4), (dict(io_dtype=_abi.SSM_F32), 3), (dict(y_dtype=7), 3),
     (dict(disc=2), 4),
+    # one batch element of fp32 y at 2^31 bytes; and one far below that whose rows up to two 64-step chunks past the
+    # end (the kernel's padding and prefetch offsets) would pass 2^32 bytes
+    (dict(seqlen=2 ** 21), 2), (dict(nheads=2 ** 17, seqlen=1), 2),
 ])
 def test_ssd_param_errors(lib, kw, code):
     p = SP(**kw)
