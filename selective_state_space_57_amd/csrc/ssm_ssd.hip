@@ -42,8 +42,8 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int kQ = 64;         // chunk length (steps)
 constexpr int kP = 64;         // head width (columns per head)
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kTiles = 10;     // lower-triangular 16x16 tiles of a 64x64 chunk
-constexpr int kMSlots = 6;     // pairs of them along s: (tb, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+// the 10 lower-triangular 16x16 tiles of a 64x64 chunk, paired along s: (tb, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr int kMSlots = 6;
 __host__ __device__ constexpr int mslot(int tb, int kk) { return tb + (tb == 3 ? 1 : 0) + kk; }
 
 // LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), stored with the 16-byte
@@ -200,6 +200,10 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, __amdgpu_buffer_rsrc_t
   }
 }
 
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 __device__ __forceinline__ void wait_vm4() { __builtin_amdgcn_s_waitcnt(0x0F74); }   // vmcnt(4)
 // Workgroup barrier for LDS data written by ds_write only: waits for this wave's LDS operations (lgkmcnt(0)), not
@@ -321,6 +325,19 @@ ssd_fwd_kernel(SsdArgs a) {
     }
   }
 
+  // LDS byte offsets of this lane's C operand pieces in the C S_prev^T product, one register each: reads that share a
+  // base register get paired into two-row reads, whose halves then have to be moved into the operand registers
+  int coff[SEGST ? 1 : NK][4][2];
+  if constexpr (!SEGST) {
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          coff[kn][tb][j] = opaque(soff<U, kSwzC>(16 * tb + l16, 4 * kn + 2 * j + (g4 >> 1)) + (g4 & 1) * 8);
+  }
+
   // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
   auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn, Scal& sc)
       __attribute__((always_inline)) {
@@ -376,12 +393,14 @@ ssd_fwd_kernel(SsdArgs a) {
     if (wave == 0) dtw = load_dt(ck + 1);
     const float* sac = sc.ac;
 
-    // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb
-    // waves 2 and 3 take three tiles, waves 0 and 1 two: wave 0 also computes the chunk's scalars (5 % faster than
-    // the other way round)
-    for (int ti = (wave + 2) & 3; ti < (SEGST ? 0 : kTiles); ti += 4) {
-      const int tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
-      const int sb = ti - tb * (tb + 1) / 2;
+    // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb.
+    // Each wave's tiles are fixed, so every wave runs its own copy with constant tile coordinates (LDS offsets fold
+    // into the instructions; only the four diagonal tiles mask).  Waves 2 and 3 take three tiles, waves 0 and 1 two:
+    // wave 0 also computes the chunk's scalars (5 % faster than the other way round).
+    auto mtile = [&](auto tic) __attribute__((always_inline)) {
+      constexpr int ti = decltype(tic)::value;
+      constexpr int tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
+      constexpr int sb = ti - tb * (tb + 1) / 2;
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
@@ -390,20 +409,36 @@ ssd_fwd_kernel(SsdArgs a) {
         acc = mfma(aB, bC, acc);
       }
       // acc[c] = CB[t = 16 tb + l16][s = 16 sb + 4 g4 + c]
-      const int t = 16 * tb + l16;
-      const float act = sac[t];
+      const float act = sac[16 * tb + l16];
       const f4 acs = *reinterpret_cast<const f4*>(&sac[16 * sb + 4 * g4]);
       const f4 phs = *reinterpret_cast<const f4*>(&sc.phi[16 * sb + 4 * g4]);
       float m[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int s = 16 * sb + 4 * g4 + c;
-        m[c] = s <= t ? acc[c] * hw_exp2(act - acs[c]) * phs[c] : 0.0f;
+        m[c] = acc[c] * hw_exp2(act - acs[c]) * phs[c];
+        if constexpr (sb == tb) m[c] = 4 * g4 + c <= l16 ? m[c] : 0.0f;
       }
       u2 hi, lo;
       split4(m[0], m[1], m[2], m[3], hi, lo);
       reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][0][lane])[sb & 1] = hi;
       reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][1][lane])[sb & 1] = lo;
+    };
+    if constexpr (!SEGST) {
+      if (wave == 0) {
+        mtile(std::integral_constant<int, 2>{});
+        mtile(std::integral_constant<int, 6>{});
+      } else if (wave == 1) {
+        mtile(std::integral_constant<int, 3>{});
+        mtile(std::integral_constant<int, 7>{});
+      } else if (wave == 2) {
+        mtile(std::integral_constant<int, 0>{});
+        mtile(std::integral_constant<int, 4>{});
+        mtile(std::integral_constant<int, 8>{});
+      } else {
+        mtile(std::integral_constant<int, 1>{});
+        mtile(std::integral_constant<int, 5>{});
+        mtile(std::integral_constant<int, 9>{});
+      }
     }
 
     // ---- inter-chunk part: Y^T[p][t] = sum_n S_prev[p][n] C[t][n], scaled by E_t = exp2(ac_t)
@@ -417,12 +452,10 @@ ssd_fwd_kernel(SsdArgs a) {
       split4(hT[2 * kn][0], hT[2 * kn][1], hT[2 * kn][2], hT[2 * kn][3], h0h, h0l);
       split4(hT[2 * kn + 1][0], hT[2 * kn + 1][1], hT[2 * kn + 1][2], hT[2 * kn + 1][3], h1h, h1l);
       const u4 hh = cat(h0h, h1h), hl = cat(h0l, h1l);
-      const int half = (g4 & 1) * 8;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const int t = 16 * tb + l16;
-        const u2 c0 = lds8(at(Cc, soff<U, kSwzC>(t, 4 * kn + (g4 >> 1)) + half));
-        const u2 c1 = lds8(at(Cc, soff<U, kSwzC>(t, 4 * kn + 2 + (g4 >> 1)) + half));
+        const u2 c0 = lds8(at(Cc, coff[kn][tb][0]));
+        const u2 c1 = lds8(at(Cc, coff[kn][tb][1]));
         const u4 bC = cat(c0, c1);
         acc[tb] = mfma(hh, bC, acc[tb]);
         acc[tb] = mfma(hl, bC, acc[tb]);
