@@ -40,37 +40,48 @@ struct CScanArgs {
 
 // sin and cos of x by Cody and Waite's reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
 // Functions", 1980): x = k pi/2 + r with pi/2 = P1 + P2 + P3 (the float nearest pi/2 and two float remainders, 72 bits
-// together), each step one fused multiply-add, so r is within about an ulp for |x| < 2^22; then Taylor polynomials
-// on |r| <= pi/4 (sin to r^9, cos to r^10: truncation below 2^-27) and the quadrant's swap and signs.  No branch:
-// the general library routine carries a large-argument path that costs even when it is not taken (6 % of the scan).
-// The phase Delta Im(A) is an fp32 product, meaningless beyond 2^22 anyway; there r is clamped so the results stay
-// bounded.
+// together), each step one fused multiply-add, so r is within about an ulp for |x| < 2^22; then polynomials on
+// |r| <= pi/4 and the quadrant's swap and signs.  k = rint(x 2/pi) comes from adding 1.5 * 2^23 in the same fused
+// multiply-add: the sum's unit is 1, so it rounds to the nearest integer, and its low mantissa bits hold k mod 4.  The
+// polynomials are minimax fits in r^2 (Lawson's iteratively reweighted least squares, fp64, on [0, pi/4]; the script
+// is sincos_fit.py): sin r / r - 1 to r^6 (relative error 3.6e-9) and cos r - 1 to r^8 (5.4e-11), each a term shorter
+// than Taylor's series for the same accuracy; evaluated in fp32 both stay within 0.9 ulp.  No branch: the general
+// library routine carries a large-argument path that costs even when it is not taken (6 % of the scan).  The phase
+// Delta Im(A) is an fp32 product, meaningless beyond 2^22 anyway; there r is clamped so the results stay bounded.
 __device__ __forceinline__ void sincos_cw(float x, float* sp, float* cp) {
   constexpr float kTwoOverPi = 0.636619772367581343f;
+  constexpr float kRound = 12582912.0f;               // 1.5 * 2^23
   constexpr float kP1 = 1.57079637050628662109375f;   // float(pi/2)
   constexpr float kP2 = -4.37113900018624283e-8f;      // float(pi/2 - P1)
   constexpr float kP3 = -1.7151245100058819e-15f;      // float(pi/2 - P1 - P2)
-  const float k = __builtin_rintf(x * kTwoOverPi);
+  const float kf = fmaf(x, kTwoOverPi, kRound);
+  const float k = kf - kRound;
   float r = fmaf(-k, kP1, x);
   r = fmaf(-k, kP2, r);
   r = fmaf(-k, kP3, r);
   r = fminf(fmaxf(r, -2.0f), 2.0f);
   const float r2 = r * r;
-  // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9!),  cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
-  float ps = fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
-  ps = fmaf(r2, ps, 1.0f / 120.0f);
-  ps = fmaf(r2, ps, -1.0f / 6.0f);
+  float ps = fmaf(r2, -1.951729937e-4f, 8.332177997e-3f);
+  ps = fmaf(r2, ps, -1.666665524e-1f);
   const float sr = fmaf(r * r2, ps, r);
-  float pc = fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
-  pc = fmaf(r2, pc, -1.0f / 720.0f);
-  pc = fmaf(r2, pc, 1.0f / 24.0f);
+  float pc = fmaf(r2, 2.439045056e-5f, -1.388676348e-3f);
+  pc = fmaf(r2, pc, 4.166662320e-2f);
   pc = fmaf(r2, pc, -0.5f);
   const float cr = fmaf(r2, pc, 1.0f);
-  // quadrant q = k mod 4: (sin, cos) = (S, C), (C, -S), (-S, -C), (-C, S)
-  const int q = static_cast<int>(k) & 3;
-  const float s0 = (q & 1) ? cr : sr, c0 = (q & 1) ? sr : cr;
-  *sp = (q & 2) ? -s0 : s0;
-  *cp = ((q + 1) & 2) ? -c0 : c0;
+  // quadrant q = k mod 4: (sin, cos) = (S, C), (C, -S), (-S, -C), (-C, S); swap on odd q, sign bits from q
+  // v_bitop3_b32 (gfx950) applies a 3-input truth table, indexed by the bits of (src0, src1, src2) taken as 0xf0,
+  // 0xcc, 0xaa: 0xca = src0 ? src1 : src2 bitwise, 0x6c = src1 ^ (src0 & src2).  The compiler spreads these selects
+  // and sign flips over twice as many plain logic instructions, hence the explicit forms.
+  const uint32_t kb = __float_as_uint(kf);
+  uint32_t swap;   // all ones on odd q (bit 0 of k, sign-extended)
+  asm("v_bfe_i32 %0, %1, 0, 1" : "=v"(swap) : "v"(kb));
+  const uint32_t su = __float_as_uint(sr), cu = __float_as_uint(cr);
+  const uint32_t s0 = __builtin_amdgcn_bitop3_b32(swap, cu, su, 0xca);
+  const uint32_t c0 = __builtin_amdgcn_bitop3_b32(swap, su, cu, 0xca);
+  const uint32_t q30 = kb << 30;   // bit 31: bit 1 of q (sin negative in quadrants 2, 3)
+  *sp = __uint_as_float(__builtin_amdgcn_bitop3_b32(q30, s0, 0x80000000u, 0x6c));
+  // bit 31 of q30 + 2^30: bit 1 of q + 1 (cos negative in quadrants 1, 2)
+  *cp = __uint_as_float(__builtin_amdgcn_bitop3_b32(q30 + 0x40000000u, c0, 0x80000000u, 0x6c));
 }
 
 // complex value (re, im) of a [..][2] io-dtype array at complex index i
