@@ -132,3 +132,29 @@ def test_complex_decode_large_exact_phases():
     st = G.to_np64(state)
     sref = np.stack([sr.real, sr.imag], axis=-1)
     assert G.rel_max(st, sref) <= 1e-6
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_complex_decode_quadrant_boundaries(sign):
+    """Pure rotations (Re(A) = 0, x = 0, Delta = 1 with softplus off, so the phase is Im(A) exactly) by phases at and
+    around the multiples k pi/2 of the reduction, k = 1..16, on both sides and with both signs: every quadrant's swap
+    and signs, and the rounding of 2x/pi to the nearest k, against the fp64 oracle at 1e-6 of rms."""
+    torch = G.torch_dev()
+    b, D, N = 1, 8, 16
+    off = np.array([0.0, 1e-6, -1e-6, 1e-3, -1e-3, 0.7853, -0.7853, 0.25], np.float64)
+    ph = (np.arange(1, N + 1)[None, :] * (np.pi / 2) + off[:, None]) * sign
+    A = np.zeros((D, N, 2), np.float32)
+    A[..., 1] = ph.astype(np.float32)
+    r = np.random.default_rng(78 if sign > 0 else 79)
+    dt = np.ones((b, D), np.float32)
+    x = np.zeros((b, D), np.float32)
+    Bc = r.standard_normal((b, N, 2), dtype=np.float32)
+    Cc = r.standard_normal((b, N, 2), dtype=np.float32)
+    h0 = r.standard_normal((b, D, N, 2), dtype=np.float32)
+    t = lambda a: torch.from_numpy(a).cuda()
+    state = t(h0.copy())
+    y = ssm.complex_state_update(state, t(x), t(dt), t(A), t(Bc), t(Cc), softplus=False, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, sr = oracle.complex_state_update(h0.astype(np.float64), x, dt, A, Bc, Cc, softplus=False)
+    assert G.rel_max(G.to_np64(y), yr) <= 1e-6
+    assert G.rel_max(G.to_np64(state), np.stack([sr.real, sr.imag], axis=-1)) <= 1e-6
