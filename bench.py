@@ -282,6 +282,24 @@ def main():
     out["hbm"]["frac_of_copy_ceiling"] = gbs / copy_gbs
     del cp_src, cp_dst
 
+    # ---- context: single launches with the 256 MB Infinity Cache evicted before each (512 MB written by a fill
+    # kernel on the same stream), median and 10th / 90th percentiles; `value` above is the mean of back-to-back steps
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(20):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold.sort()
+    out["cold"] = {"launches": len(cold), "median_ms": cold[len(cold) // 2], "p10_ms": cold[len(cold) // 10],
+                   "p90_ms": cold[(9 * len(cold)) // 10], "elements_per_s_at_median": elems / (cold[len(cold) // 2] * 1e-3),
+                   "flush": "512 MB written by a fill kernel before each launch"}
+
     # ---- the same forward with the block's causal convolution (width 4) + SiLU fused in front of the scan
     if not args.no_conv:
         from selective_state_space_57_amd import _abi
