@@ -314,7 +314,34 @@ ssd_fwd_kernel(SsdArgs a) {
   stage_rows<U>(sB0, rB, stB, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
   if constexpr (!SEGST) stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
   stage_rows<8>(sX0, rx, stX, wave, static_cast<uint32_t>(c0 * kQ) * x_row, x_row);
-  uint32_t dtw = wave == 0 ? load_dt(c0) : 0u;
+  // Per-step scalars of a chunk (Delta, phi, the running sum, decay weights), computed by every wave from dt it loads
+  // itself, and stored by wave 0.  Chunk ck computes those of chunk ck + 1 after its state update, whose matrix
+  // products run meanwhile, so that the dependent chain (softplus, the prefix sum across the wave) is not on the path
+  // to the chunk barrier; the next chunk's barrier publishes them.  The copy written was last read in the chunk
+  // before, whose readers have all passed the current chunk's barrier.
+  auto scalars = [&](int c, uint32_t dtv, Scal& out) __attribute__((always_inline)) {
+    const float u = bf_lo(dtv) + bias;
+    float dl = a.softplus ? softplus(u) : u;
+    dl = (c * kQ + lane < L) ? dl : 0.0f;
+    float ph = dl;
+    if (ZOH) {
+      const float e = dl * Ah;
+      ph = Ah == 0.0f ? dl : expm1_from(e, hw_exp2(e * kLog2e)) / Ah;
+    }
+    const float cum = wave_incl_scan(dl, lane);
+    const float acv = cum * A2;
+    const float ac63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acv), 63));
+    if constexpr (SEGST) {
+      if (c < c1) dsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
+    }
+    const float wv = ph * hw_exp2(ac63 - acv);
+    if (wave == 0) {
+      out.ac[lane] = acv;
+      out.phi[lane] = ph;
+      out.w[lane] = wv;
+    }
+  };
+  scalars(c0, load_dt(c0), sSc[0]);
   if constexpr (!SEGST) {
     if (wave == 0) {   // the halves of the pair slots whose second tile lies above the diagonal stay zero
 #pragma unroll
@@ -339,41 +366,23 @@ ssd_fwd_kernel(SsdArgs a) {
   }
 
   // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
-  auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn, Scal& sc)
-      __attribute__((always_inline)) {
+  auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn, Scal& sc,
+                   Scal& scn) __attribute__((always_inline)) {
     const int t0 = ck * kQ;
     const uint16_t* Cc = sC;
-    // This wave's copies of chunk ck and its dt have landed.  The memory counter completes in issue order, and the
+    // This wave's copies of chunk ck have landed.  The memory counter completes in issue order, and the
     // last 4 operations of a chunk are the 4 output stores (one per 16-step block, always issued): after the first
     // chunk of the full pass those may stay in flight.
     if (SEGST || ck == c0)
       wait_vm0();
     else
       wait_vm4();
-    if (wave == 0) {
-      // per-step scalars, once for the workgroup: Delta, phi, running sum, decay weights.  The barrier below publishes
-      // them; this copy was last read two chunks ago, before the barrier of the chunk in between.  Computing them in
-      // every wave cost 4x the dt requests and measured 3 % slower.  Every wave waits for them at that barrier, so
-      // wave 0 takes issue priority over the other workgroup's wave on its SIMD meanwhile (1-2 % faster).
-      __builtin_amdgcn_s_setprio(2);
-      const float u = bf_lo(dtw) + bias;
-      float dl = a.softplus ? softplus(u) : u;
-      dl = (t0 + lane < L) ? dl : 0.0f;
-      float ph = dl;
-      if (ZOH) {
-        const float e = dl * Ah;
-        ph = Ah == 0.0f ? dl : expm1_from(e, hw_exp2(e * kLog2e)) / Ah;
-      }
-      const float cum = wave_incl_scan(dl, lane);
-      const float acv = cum * A2;
-      const float ac63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acv), 63));
-      if constexpr (SEGST) dsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
-      sc.ac[lane] = acv;
-      sc.phi[lane] = ph;
-      sc.w[lane] = ph * hw_exp2(ac63 - acv);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();                        // chunk ck is in LDS everywhere; chunk ck-1 is finished by every wave
+    // dt of the next chunk, before the barrier: it is then the oldest load still in flight where it is used
+    const uint32_t dtv = load_dt(ck + 1);
+    // Chunk ck and its scalars are in LDS everywhere; chunk ck-1 is finished by every wave.  No wave reads another's
+    // global stores, so the barrier leaves the previous chunk's output stores in flight (a workgroup fence would wait
+    // for them).
+    lds_barrier();
     // (issued before the next chunk's copies: the wait for z then leaves those in flight)
     // z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
     u2 zo[4];
@@ -390,13 +399,11 @@ ssd_fwd_kernel(SsdArgs a) {
     // the next chunk's copies (past the last chunk they read zeros into a buffer nobody reads)
     stage_rows<U>(Bn, rB, stB, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
     stage_rows<8>(Xn, rx, stX, wave, static_cast<uint32_t>(t0 + kQ) * x_row, x_row);
-    if (wave == 0) dtw = load_dt(ck + 1);
     const float* sac = sc.ac;
 
     // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb.
     // Each wave's tiles are fixed, so every wave runs its own copy with constant tile coordinates (LDS offsets fold
-    // into the instructions; only the four diagonal tiles mask).  Waves 2 and 3 take three tiles, waves 0 and 1 two:
-    // wave 0 also computes the chunk's scalars (5 % faster than the other way round).
+    // into the instructions; only the four diagonal tiles mask).  Waves 2 and 3 take three tiles, waves 0 and 1 two.
     auto mtile = [&](auto tic) __attribute__((always_inline)) {
       constexpr int ti = decltype(tic)::value;
       constexpr int tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
@@ -501,6 +508,7 @@ ssd_fwd_kernel(SsdArgs a) {
         hT[nb] = st;
       }
     }
+    scalars(ck + 1, dtv, scn);              // the next chunk's, while the state update's products run
     if constexpr (SEGST) return;            // the zero-start pass only carries the state
     lds_barrier();                          // M tiles are in LDS; every wave is done with C
     stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
@@ -551,8 +559,8 @@ ssd_fwd_kernel(SsdArgs a) {
     }
     };
   for (int ck = c0; ck < c1; ck += 2) {
-    chunk(ck, sB0, sX0, sB1, sX1, sSc[0]);
-    if (ck + 1 < c1) chunk(ck + 1, sB1, sX1, sB0, sX0, sSc[1]);
+    chunk(ck, sB0, sX0, sB1, sX1, sSc[0], sSc[1]);
+    if (ck + 1 < c1) chunk(ck + 1, sB1, sX1, sB0, sX0, sSc[1], sSc[0]);
   }
 
   if constexpr (SEGST) {
