@@ -231,3 +231,43 @@ def test_conv_scan_training_chain():
         e = G.rel_max(G.to_np64(gc[k]), gcr[rk])
         assert e <= 1e-4, (k, e)
     assert G.rel_max(G.to_np64(gs["dA"]), gsr["dA"]) <= 1e-4
+
+
+def test_conv1d_full_size_sampled():
+    """The convolution on its own and its backward at the size the benchmark times (4 x 5120 x 4096, width 4, SiLU,
+    bf16 x, u, du and dx, the same launch configurations): fp32-output runs against the oracle on sampled channels,
+    and the bf16 outputs equal to their round-to-nearest-even over the whole tensors."""
+    torch = G.torch_dev()
+    w = I.WORKLOADS[2]
+    x = I.scan_inputs(w)["x"]
+    cv = I.conv_params(w, 4)
+    du_bits = I.cotangents(w)["dy"]   # bf16, as the benchmark's du
+    dd = G.to_dev({"x": x, "du": du_bits})
+    dc = G.to_dev(cv)
+    u32 = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], None, activation=True, u_dtype=torch.float32)
+    u16 = ssm.conv1d_fwd(dd["x"], dc["conv_w"], dc["conv_b"], None, activation=True, u_dtype=torch.bfloat16)
+    g32 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], dd["du"].to(torch.float32), dc["conv_b"], None, None, activation=True)
+    g16 = ssm.conv1d_bwd(dd["x"], dc["conv_w"], dd["du"], dc["conv_b"], None, None, activation=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16.to(torch.float32).cpu().numpy(), G.bf16_rne(u32.cpu().numpy()))
+    assert np.array_equal(g16["dx"].to(torch.float32).cpu().numpy(), G.bf16_rne(g32["dx"].cpu().numpy()))
+    assert torch.equal(g16["dweight"], g32["dweight"]) and torch.equal(g16["dbias"], g32["dbias"])
+    x64, du64 = I.to_f64(x, w.io), I.to_f64(du_bits, w.io)
+    w64, b64 = cv["conv_w"].astype(np.float64), cv["conv_b"].astype(np.float64)
+    chans = G.sample_channels(w.batch, w.dim, 16, seed=7)
+    un, dxn = G.to_np64(u32), G.to_np64(g32["dx"])
+    dwn, dbn = G.to_np64(g32["dweight"]), G.to_np64(g32["dbias"])
+    got_u, ref_u, got_dx, ref_dx, got_dw, ref_dw, got_db, ref_db = [], [], [], [], [], [], [], []
+    for di in sorted({c[1] for c in chans}):
+        ur, _ = oracle.conv1d(x64[:, di:di + 1], w64[di:di + 1], bias=b64[di:di + 1], silu=True)
+        gr = oracle.conv1d_bwd(x64[:, di:di + 1], w64[di:di + 1], du64[:, di:di + 1], bias=b64[di:di + 1], silu=True)
+        got_u.append(un[:, di]); ref_u.append(ur[:, 0])
+        got_dx.append(dxn[:, di]); ref_dx.append(gr["dx"][:, 0])
+        got_dw.append(dwn[di]); ref_dw.append(gr["dw"][0])
+        got_db.append(dbn[di]); ref_db.append(gr["dbias"][0])
+    # fp32 evaluation: four products, the bias, SiLU's exponential and reciprocal, about an ulp each, so up to about
+    # 8 x 2^-24 of |u|; over millions of outputs the largest |u| are several times rms(u): the fp32 bar, 1e-5 of rms
+    assert G.rel_max(np.stack(got_u), np.stack(ref_u)) <= G.TOL_F32
+    assert G.rel_max(np.stack(got_dx), np.stack(ref_dx)) <= 1e-5
+    assert G.rel_max(np.stack(got_dw), np.stack(ref_dw)) <= 1e-5
+    assert G.rel_max(np.array(got_db), np.array(ref_db)) <= 1e-5

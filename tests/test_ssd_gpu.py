@@ -193,3 +193,32 @@ def test_ssd_zero_A_heads(disc):
     yr, hr = ref(d, disc=disc)
     assert G.rel_max(G.to_np64(y), yr) <= TOL_SSD
     assert G.rel_max(G.to_np64(hf), hr) <= TOL_SSD
+
+
+def test_ssd_decode_full_size_sampled():
+    """The decode step at the size the benchmark times (256 sequences x 80 heads of 64, N = 128, bf16 io, the 671 MB
+    fp32 state updated in place), two consecutive steps; the oracle recomputes a sample of sequences."""
+    torch = G.torch_dev()
+    w = I.SSD_WORKLOADS[2]
+    first = I.ssd_inputs(w, with_h0=True)
+    h0 = first.pop("h0")
+    steps = [first, I.ssd_inputs(w, step=1)]
+    st = torch.from_numpy(h0).cuda()
+    ys = []
+    for q in steps:   # decode workloads have no L axis: x (b, H, P), dt (b, H), B and C (b, G, N)
+        dq = G.to_dev(q)
+        ys.append(ssm.ssd_state_update(st, dq["x"], dq["dt"], dq["A"], dq["B"], dq["C"], dt_bias=dq["dt_bias"],
+                                       Dskip=dq["Dskip"], z=dq["z"], y_dtype=torch.float32))
+    torch.cuda.synchronize()
+    sel = [0, 97, 255]
+    sr = h0[sel].astype(np.float64)
+    for i, q in enumerate(steps):
+        f = I.as_f64(q)
+        fl = lambda k: None if f[k] is None else f[k][sel]
+        yr, sr = oracle.ssd_state_update(sr, fl("x"), fl("dt"), f["A"], fl("B"), fl("C"), dt_bias=f["dt_bias"],
+                                         Dskip=f["Dskip"], z=fl("z"))
+        e = G.rel_max(G.to_np64(ys[i])[sel], yr)
+        print("ssd decode full size step %d: y err %.2e" % (i, e), flush=True)
+        assert e <= 1e-5, (i, e)
+    assert G.rel_max(G.to_np64(st[sel]), sr) <= 1e-5
+    assert bool(torch.isfinite(st).all())
