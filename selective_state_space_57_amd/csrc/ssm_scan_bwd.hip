@@ -436,7 +436,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     TG* const qdz = GATE ? static_cast<TG*>(p.dz) + obase : nullptr;
     const int64_t d = chan(q);
     const bool chv = d < p.dim;
-    const int64_t bd = b * p.dim + d;
     const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
     const float Ap = An * kLog2e;
     const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
