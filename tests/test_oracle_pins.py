@@ -183,6 +183,11 @@ MUTANTS = [
      "if (z) acc *= z[i] / (1.0 + exp(z[i]));"),
     ("ssd_decode_zoh_no_div", r"expm1\(delta \* Ah\) / Ah\);(\s+const double\* Bt = B \+ \(b \* G)",
      r"expm1(delta * Ah));\1"),
+    ("bwd_dB_no_coef", r"dB\[b \* N \* L \+ n \* L \+ t\] \+= g\[n\] \* coef \* xv;",
+     "dB[b * N * L + n * L + t] += g[n] * xv;"),
+    ("bwd_dA_decay_no_delta", r"hprev \* abar \* delta\);", "hprev * abar);"),
+    ("bwd_dD_ignores_gate", r"accD \+= ds \* xv;", "accD += dyv * xv;"),
+    ("bwd_dz_no_preactivation", r"dz\[ch \* L \+ t\] = dyv \* S\[t\] \* ", "dz[ch * L + t] = dyv * "),
 ]
 
 
