@@ -188,6 +188,9 @@ MUTANTS = [
     ("bwd_dA_decay_no_delta", r"hprev \* abar \* delta\);", "hprev * abar);"),
     ("bwd_dD_ignores_gate", r"accD \+= ds \* xv;", "accD += dyv * xv;"),
     ("bwd_dz_no_preactivation", r"dz\[ch \* L \+ t\] = dyv \* S\[t\] \* ", "dz[ch * L + t] = dyv * "),
+    ("bwd_dbias_dropped", r"if \(ddt_bias\) ddt_bias\[d\] = sb;", "if (ddt_bias) ddt_bias[d] = 0.0;"),
+    ("bwd_dh0_zero", r"dh0\[ch \* N \+ n\] = g\[n\];", "dh0[ch * N + n] = 0.0;"),
+    ("conv_bwd_dbias_dropped", r"if \(dbias\) dbias\[d\] = sb;", "if (dbias) dbias[d] = 0.0;"),
 ]
 
 
