@@ -245,7 +245,9 @@ def pin_zoh_euler(orc):
         ye, _ = orc.scan(*args, disc=EULER_B)
         delta = math.log1p(math.exp(u)) if u < 30 else u
         ratio = math.expm1(delta * a) / (delta * a)
-        assert abs(yz[0, 0, 0] / ye[0, 0, 0] - ratio) < 1e-14, ("P8", u, a)
+        with np.errstate(divide="ignore", invalid="ignore"):   # a broken oracle may give 0 / 0; it then fails here
+            got = yz[0, 0, 0] / ye[0, 0, 0]
+        assert abs(got - ratio) < 1e-14, ("P8", u, a)
         if delta < 1e-3:
             assert abs(ratio - (1 + delta * a / 2)) < (delta * a) ** 2 + 4e-16
     # A == 0 takes the limit Delta * B
