@@ -191,6 +191,13 @@ MUTANTS = [
     ("bwd_dbias_dropped", r"if \(ddt_bias\) ddt_bias\[d\] = sb;", "if (ddt_bias) ddt_bias[d] = 0.0;"),
     ("bwd_dh0_zero", r"dh0\[ch \* N \+ n\] = g\[n\];", "dh0[ch * N + n] = 0.0;"),
     ("conv_bwd_dbias_dropped", r"if \(dbias\) dbias\[d\] = sb;", "if (dbias) dbias[d] = 0.0;"),
+    # the SSD decode's own copies of lines the scan shares (the patterns above rewrite both)
+    ("ssd_decode_group_index", r"const int64_t g = h / hpg;(\s+const double Ah = A\[h\];\s+const double u = dt\[b \* H)",
+     r"const int64_t g = h % G;\1"),
+    ("ssd_decode_abar_sign", r"const double abar = exp\(delta \* Ah\);(\s+const double coef = disc == 0 \? delta : "
+     r"\(Ah == 0\.0 \? delta : expm1\(delta \* Ah\) / Ah\);\s+const double\* Bt = B \+ \(b \* G \+ g\) \* N;)",
+     r"const double abar = exp(-delta * Ah);\1"),
+    ("ssd_decode_C_from_B", r"const double\* Ct = C \+ \(b \* G \+ g\) \* N;", "const double* Ct = B + (b * G + g) * N;"),
 ]
 
 
