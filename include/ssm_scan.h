@@ -251,8 +251,10 @@ int ssm_ssd_fwd_plan_segments(const ssm_ssd_params* p);
  * x, B, C, z, y, h0 and h_final must be 16-byte aligned.  workspace: device buffer of at least
  * ssm_ssd_fwd_workspace_bytes(p) bytes, 16-byte aligned (NULL if 0 are needed): with more than one segment a first
  * pass writes each segment's end state from a zero start there, and every segment starts from h0 carried through the
- * segments before it.  Errors as for ssm_scan_fwd, plus SSM_ERR_DTYPE for io_dtype != SSM_BF16 and
- * SSM_ERR_UNSUPPORTED for headdim != 64, dstate not in {64, 128, 256} or negative segments.
+ * segments before it.  Errors as for ssm_scan_fwd, plus SSM_ERR_DTYPE for io_dtype != SSM_BF16,
+ * SSM_ERR_UNSUPPORTED for headdim != 64, dstate not in {64, 128, 256} or negative segments, and SSM_ERR_SHAPE when
+ * one batch element reaches 2^31 bytes (x or y counted at 4 bytes a value: seqlen * nheads * 64 * 4; B or C:
+ * seqlen * ngroups * dstate * 2) or (seqlen + 128) steps of either reach 2^32 bytes (device offsets are 32-bit).
  */
 ssm_status ssm_ssd_fwd(const ssm_ssd_params* p, const void* x, const void* dt, const float* dt_bias, const float* A,
                        const void* B, const void* C, const float* Dskip, const void* z, const float* h0, void* y,
