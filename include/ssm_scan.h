@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,         /* a required pointer is NULL */
-  SSM_ERR_SHAPE = 2,        /* batch/dim/seqlen < 1, dstate outside [1, 16], sizes that overflow the grid */
+  SSM_ERR_SHAPE = 2,        /* batch/dim/seqlen < 1, dstate outside [1, 16], batch > 65535, seqlen > 2^25
+                               (32-bit per-lane offsets), sizes that overflow the grid (SSD limits: ssm_ssd_fwd) */
   SSM_ERR_DTYPE = 3,        /* unknown io_dtype / y_dtype */
   SSM_ERR_UNSUPPORTED = 4,  /* unknown disc or dt_softplus value, negative segments */
   SSM_ERR_ALIGN = 5,        /* a pointer not aligned to its element size */
