@@ -39,8 +39,9 @@ struct CScanArgs {
 };
 
 // sin and cos of x by Cody and Waite's reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
-// Functions", 1980): x = k pi/2 + r with pi/2 = P1 + P2 + P3 (the float nearest pi/2 and two float remainders, 72 bits
-// together), each step one fused multiply-add, so r is within about an ulp for |x| < 2^22; then polynomials on
+// Functions", 1980): x = k pi/2 + r with pi/2 ~ P1 + P2 (the float nearest pi/2 and the float nearest the remainder,
+// 48 bits together), each step one fused multiply-add; for |x| < 2^22 (|k| < 2.7e6) r is within its rounding plus
+// |k| 1.7e-15 < 5e-9 of the exact reduced argument, under 0.1 ulp of the results; then polynomials on
 // |r| <= pi/4 and the quadrant's swap and signs.  k = rint(x 2/pi) comes from adding 1.5 * 2^23 in the same fused
 // multiply-add: the sum's unit is 1, so it rounds to the nearest integer, and its low mantissa bits hold k mod 4.  The
 // polynomials are minimax fits in r^2 (Lawson's iteratively reweighted least squares, fp64, on [0, pi/4]; the script
@@ -53,12 +54,10 @@ __device__ __forceinline__ void sincos_cw(float x, float* sp, float* cp) {
   constexpr float kRound = 12582912.0f;               // 1.5 * 2^23
   constexpr float kP1 = 1.57079637050628662109375f;   // float(pi/2)
   constexpr float kP2 = -4.37113900018624283e-8f;      // float(pi/2 - P1)
-  constexpr float kP3 = -1.7151245100058819e-15f;      // float(pi/2 - P1 - P2)
   const float kf = fmaf(x, kTwoOverPi, kRound);
   const float k = kf - kRound;
   float r = fmaf(-k, kP1, x);
   r = fmaf(-k, kP2, r);
-  r = fmaf(-k, kP3, r);
   r = fminf(fmaxf(r, -2.0f), 2.0f);
   const float r2 = r * r;
   float ps = fmaf(r2, -1.951729937e-4f, 8.332177997e-3f);
