@@ -23,8 +23,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-VALU_PEAK_TFLOPS = 78.6          # non-packed fp32 FMA: 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz
-TRANS_SLOTS = 2                  # issue cost of v_exp/v_log/v_rcp in FMA slots on gfx950 (half rate)
+# VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 3.93e13 lane-slots/s for non-packed fp32 (one add, multiply or
+# FMA per lane and slot; packed FP32 is not used).  Reported in units of 10^12 lane-slots/s.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Issue cost of one v_exp_f32 / v_log_f32 / v_rcp_f32 in VALU slots.  The issue-rate probe
+# (selective_state_space_57_amd/csrc/issue_probe.hip, run by every bench.py call: `issue_rates` in the JSON line)
+# measures it on the box as (FMA rate) / (exp rate); on MI355X it reads 2.0-2.1, and an exp interleaved with FMAs in
+# one wave, or issued by another wave of the same SIMD, costs the same two slots (no co-issue).  The record is in
+# profiles/issue_rates_mi355x.md.
+TRANS_SLOTS = 2
 
 
 def scan_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
@@ -35,36 +42,162 @@ def scan_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
     return seq + bc + par + b * D * N * 4
 
 
-def scan_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
-    """fp32 work per (b, d, t) in FMA-slot units x 2 FLOP:
-    per state n: Delta*A (1), exp (2 slots), (Delta x)*B (1), h = a h + b (1 FMA), y += C h (1 FMA)  -> 6 slots;
-    per element: dt + bias (1), softplus = exp + log + rcp (6) + 5 ops, Delta*x (1), D*x (1), silu = exp + rcp (4)
-    + 3 ops.  Each slot is counted as 2 FLOP so that the figure compares with the 78.6 TFLOP/s FMA peak."""
-    per_elem = 6 * N + 1 + 11 + 1 + (1 if dskip else 0) + (7 if gate else 0)
-    return 2.0 * per_elem * b * D * L
+SOFTPLUS_SLOTS = 13   # -|u| log2(e), exp (2), 1 + v, w - 1, v - (w - 1), 1 - v, log2 (2), x ln 2, fma, max(u, 0), +
+SILU_SLOTS = 7        # -z log2(e), exp (2), 1 + e, rcp (2), z r
 
 
-def complex_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
-    """Complex-A forward per (b, d, t) in FMA-slot units x 2: per state Delta*Re(A), exp (2), sin + cos (4),
-    (Delta x) B (2), the complex update (4), Re(C h) (2) and its sum (1) = 16; per element as the real scan (25)."""
-    per_elem = 16 * N + 1 + 11 + 1 + (1 if dskip else 0) + (7 if gate else 0)
-    return 2.0 * per_elem * b * D * L
+def scan_elem_slots(N, gate=True, dskip=True, softplus=True):
+    """Algorithmic VALU issue slots of the forward scan per (b, d, t) element (transcendental = TRANS_SLOTS).
+    Per state n: Delta*A' (1), exp (2), (Delta x)*B (1), h = a h + b (1 FMA), y += C h (1 FMA)  -> 6;
+    per element: dt + bias (1), softplus (13), Delta*x (1), D*x (1 FMA), silu (7) and the gate's product (1)."""
+    per_elem = 1 + (SOFTPLUS_SLOTS if softplus else 0) + 1 + (1 if dskip else 0) + (SILU_SLOTS + 1 if gate else 0)
+    return (4 + TRANS_SLOTS) * N + per_elem
 
 
-def conv_algorithmic_flops(b, D, L, width=4):
-    """The causal convolution + SiLU in front of the scan, per (b, d, t): width FMAs, SiLU = exp + rcp (4 slots) + 2."""
-    return 2.0 * (width + 6) * b * D * L
+def scan_algorithmic_slots(b, D, L, N, gate=True, dskip=True, softplus=True):
+    return float(scan_elem_slots(N, gate, dskip, softplus)) * b * D * L
 
 
-def bwd_algorithmic_flops(b, D, L, N, gate=True, dskip=True):
-    """fp32 work of the backward per (b, d, t), in FMA-slot units x 2 FLOP (same convention as the forward).
+def complex_algorithmic_slots(b, D, L, N, gate=True, dskip=True):
+    """Complex-A forward per (b, d, t): per state Delta*Re(A), exp (2), sin + cos (4), (Delta x) B (2), the complex
+    update (4), Re(C h) (2) and its sum (1) = 16; per element as the real scan."""
+    return float(16 * N + scan_elem_slots(0, gate, dskip)) * b * D * L
+
+
+def conv_algorithmic_slots(b, D, L, width=4):
+    """The causal convolution + SiLU in front of the scan, per (b, d, t): width FMAs, SiLU (7)."""
+    return float(width + SILU_SLOTS) * b * D * L
+
+
+def bwd_algorithmic_slots(b, D, L, N, gate=True, dskip=True):
+    """VALU issue slots of the backward per (b, d, t) (same convention as the forward).
     Per state n: zero-start chunk pass 8 (Delta*A, exp 2, (Delta x)*B, h FMA, decay product, C*ds, lambda FMA);
     recomputation 5 (Delta*A, exp 2, (Delta x)*B, h FMA); adjoint 2 (g += C ds, g *= a); dA 3 (a h_prev, g u,
     += Delta); dx / dDelta terms 2 (g B, A g u) and their sums over n 2; dB / dC 2 FMA; with the gate C h and its sum 2.
-    Per element: softplus twice (11 each), sigmoid(u) 4, silu twice (7 each), dz 4, dx / dDelta / du 4."""
+    Per element: softplus twice (13 each), sigmoid(u) 4, silu twice (7 each), dz 4, dx / dDelta / du 4."""
     per_n = 8 + 5 + 2 + 3 + 4 + 2 + (2 if gate else 0)
-    per_elem = 11 * 2 + 4 + (7 * 2 + 4 if gate else 0) + 4 + (2 if dskip else 0)
-    return 2.0 * (per_n * N + per_elem) * b * D * L
+    per_elem = SOFTPLUS_SLOTS * 2 + 4 + (SILU_SLOTS * 2 + 4 if gate else 0) + 4 + (2 if dskip else 0)
+    return float(per_n * N + per_elem) * b * D * L
+
+
+def alu_roofline(slots, ms, kernel, traffic=None, extra=None):
+    """The ALU roofline object: algorithmic lane-slots per launch / launch time against VALU_PEAK_TSLOTS."""
+    ach = slots / (ms * 1e-3) / 1e12
+    r = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_TSLOTS, "unit": "Tslot/s", "frac": ach / VALU_PEAK_TSLOTS,
+         "traffic": traffic, "kernel": kernel, "algorithmic_slots": slots,
+         "slot_model": "one fp32 add / multiply / FMA per lane = 1 slot, one exp / log / rcp = %d slots; peak = 256 CU "
+                       "x 4 SIMD x 16 lanes x 2.4 GHz (non-packed fp32)" % TRANS_SLOTS}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def hbm_roofline(nbytes, ms, traffic=None, kernel=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "kernel": kernel, "algorithmic_bytes": nbytes}
+
+
+PROBE_KINDS = (("fma", 0), ("exp", 1), ("mix_exp_fma_1_1", 2), ("mix_exp_fma_1_3", 3), ("log", 4), ("rcp", 5),
+               ("split_waves_exp_fma", 6), ("mul_dpp_bcast", 7), ("lds_read_b128", 8),
+               ("lds_read_b128_row_broadcast", 9), ("lds_write_b32", 10), ("lds_read_b32", 11),
+               ("scan_step_dpp", 12), ("scan_step_plain", 13), ("vmem_load_b128", 14),
+               ("vmem_load_b128_row_broadcast", 15), ("lds_write_b64", 16), ("lds_write_b128", 17))
+# bytes one wave moves per LDS (or vector-memory) instruction of each memory probe kind
+PROBE_LDS_BYTES = {8: 64 * 16, 9: 64 * 16, 10: 64 * 4, 11: 64 * 4, 14: 64 * 16, 15: 64 * 16, 16: 64 * 8,
+                   17: 64 * 16}
+
+
+def issue_rates(torch, dev, stream, iters=4000, reps=3):
+    """Run the issue-rate probe (libssm57_probe.so): per kernel the lane-operations retired per second, the exp cost
+    in FMA slots, whether exps and FMAs overlap, and the shader clock under load (s_memtime over s_memrealtime)."""
+    import ctypes
+    path = os.path.join(ROOT, "selective_state_space_57_amd", "libssm57_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.ssm_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ssm_probe_launch.restype = ctypes.c_int
+    lib.ssm_probe_ops_per_iter.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int * 3)]
+    grid = lib.ssm_probe_grid()
+    lanes = grid * 256
+    out = torch.empty(lanes, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    wall_khz = lib.ssm_probe_wallclock_khz()
+    res = {}
+    for name, kind in PROBE_KINDS:
+        for _ in range(2):
+            rc = lib.ssm_probe_launch(kind, iters, out.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+            assert rc == 0, ("probe launch", name, rc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            lib.ssm_probe_launch(kind, iters, out.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        ops = (ctypes.c_int * 3)()
+        lib.ssm_probe_ops_per_iter(kind, ctypes.byref(ops))
+        c = clk.view(grid, 2).double()
+        ghz = float((c[:, 0] / c[:, 1].clamp(min=1)).median()) * wall_khz * 1e-6 if wall_khz else None
+        waves = lanes // 64
+        cycles_per_simd = ms * 1e-3 * (ghz or 2.4) * 1e9
+        if kind in PROBE_LDS_BYTES:   # LDS bytes per clock per CU
+            r = {"ms": ms, "shader_clock_GHz": ghz, "instructions_per_wave": ops[0] * iters,
+                 "bytes_per_clock_per_CU": ops[0] * iters * waves * PROBE_LDS_BYTES[kind] / 256 / cycles_per_simd,
+                 "cycles_per_wave_instruction_per_CU": cycles_per_simd * 256 / (ops[0] * iters * waves)}
+        elif kind in (12, 13):        # SIMD cycles per wave and state step
+            r = {"ms": ms, "shader_clock_GHz": ghz,
+                 "cycles_per_wave_step": cycles_per_simd * 1024 / (waves * iters * ops[1])}
+        else:
+            r = {"ms": ms, "fma_lane_ops_per_s": ops[0] * iters * lanes / (ms * 1e-3),
+                 "trans_lane_ops_per_s": ops[1] * iters * lanes / (ms * 1e-3), "shader_clock_GHz": ghz,
+                 "cycles_per_wave_instruction": cycles_per_simd * 1024 / (waves * iters * (ops[0] + ops[1] + ops[2]))}
+        res[name] = r
+    t = {k: v["ms"] for k, v in res.items()}
+    fma = res["fma"]["fma_lane_ops_per_s"]
+    expr = res["exp"]["trans_lane_ops_per_s"]
+    summary = {
+        "fma_lane_ops_per_s": fma, "exp_lane_ops_per_s": expr,
+        "fma_frac_of_issue_peak": fma / (VALU_PEAK_TSLOTS * 1e12),
+        "exp_cost_in_fma_slots": fma / expr,
+        "log_cost_in_fma_slots": fma / res["log"]["trans_lane_ops_per_s"],
+        "rcp_cost_in_fma_slots": fma / res["rcp"]["trans_lane_ops_per_s"],
+        # equal work split two ways; 1.0 = the two kinds take turns on one issue port, max/sum = they overlap fully
+        "mix_1_1_time_over_sum": t["mix_exp_fma_1_1"] / (t["fma"] + t["exp"]),
+        "mix_1_1_time_over_max": t["mix_exp_fma_1_1"] / max(t["fma"], t["exp"]),
+        "split_waves_time_over_mean": t["split_waves_exp_fma"] / (0.5 * (t["fma"] + t["exp"])),
+        "split_waves_time_over_max_half": t["split_waves_exp_fma"] / (0.5 * max(t["fma"], t["exp"])),
+        "mul_dpp_over_fma_rate": res["mul_dpp_bcast"]["fma_lane_ops_per_s"] / fma,
+        "cycles_per_wave_instruction": {k: res[k]["cycles_per_wave_instruction"]
+                                        for k in ("fma", "exp", "mul_dpp_bcast")},
+        "memory_bytes_per_clock_per_CU": {k: res[k]["bytes_per_clock_per_CU"]
+                                          for k in ("lds_read_b128", "lds_read_b128_row_broadcast", "lds_write_b32",
+                                                    "lds_write_b64", "lds_write_b128", "vmem_load_b128",
+                                                    "vmem_load_b128_row_broadcast")},
+        "scan_step_cycles_per_wave": {k: res[k]["cycles_per_wave_step"] for k in ("scan_step_dpp", "scan_step_plain")},
+        "shader_clock_GHz_under_fma_load": res["fma"]["shader_clock_GHz"],
+        "wall_clock_kHz": wall_khz, "iters": iters, "lanes": lanes,
+        "kernels": res,
+    }
+    return summary
+
+
+def time_launches(torch, stream, fn, n):
+    """n back-to-back launches with an event between consecutive ones: (mean ms, sorted per-launch ms)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    return evs[0].elapsed_time(evs[n]) / n, per
+
+
+def pct(per):
+    """p10 / median / p90 of a sorted list."""
+    n = len(per)
+    return {"p10_ms": per[n // 10], "median_ms": per[n // 2], "p90_ms": per[min(n - 1, (9 * n) // 10)]}
 
 
 def bwd_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
@@ -161,6 +294,101 @@ def host_cores():
     return max(1, min(n, 16))
 
 
+# launches timed per workload leg (each leg also does two untimed warm-up launches)
+LEG_STEPS = {"tiny-s6-fp32": 100, "mamba130m-layer": 50, "mamba2.8b-layer": 50, "million-length": 10}
+# the oracle's bounded sample per workload leg: channels (of b * D, taken from the start) or None for all
+LEG_CPU_CHANNELS = {"tiny-s6-fp32": None, "mamba130m-layer": None, "mamba2.8b-layer": None, "million-length": 64}
+
+
+def workload_leg(torch, np, ssm, I, up, w, dev, stream, steps=None, cpu=True, log=None):
+    """Forward scan of one workload as the product runs it (y in the io dtype): per-launch times, elements/s, the HBM
+    and ALU roofline fractions, and, with cpu, the fp64 oracle timed on a bounded sample of the same inputs (which
+    also checks the fp32-y result on that sample)."""
+    b, D, L, N = w.batch, w.dim, w.seqlen, w.dstate
+    io_bytes = 4 if w.io == I.F32 else 2
+    if log:
+        log("workload %s: generating inputs" % w.name)
+    host = I.scan_inputs(w)
+    d = {k: up(v) for k, v in host.items()}
+    ydt = torch.float32 if w.io == I.F32 else torch.bfloat16
+    y = torch.empty((b, D, L), dtype=ydt, device=dev)
+    hf = torch.empty((b, D, N), dtype=torch.float32, device=dev)
+    p = ssm.make_params(b, D, L, N, ssm.io_code(ydt), ssm.io_code(ydt))
+    nseg = ssm.plan_segments(p)
+    ws_n = ssm.workspace_bytes(p)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    from selective_state_space_57_amd import _abi
+
+    # arguments marshalled once (the binding's per-call checks would leave the GPU idle between short launches)
+    sargs = (d["x"].data_ptr(), d["dt"].data_ptr(), d["dt_bias"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
+             d["C"].data_ptr(), d["Dskip"].data_ptr(), d["z"].data_ptr(), 0, y.data_ptr(), hf.data_ptr(),
+             ws.data_ptr() if ws_n else 0, ws_n, stream.cuda_stream)
+
+    def step():
+        st = _abi.scan_fwd_raw(p, *sargs)
+        if st:
+            _abi.check(st)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    n = steps or LEG_STEPS.get(w.name, 20)
+    ms, per = time_launches(torch, stream, step, n)
+    elems = b * D * L
+    nbytes = scan_algorithmic_bytes(b, D, L, N, io_bytes, w.gate, w.dskip)
+    slots = scan_algorithmic_slots(b, D, L, N, w.gate, w.dskip)
+    io = "f32" if w.io == I.F32 else "bf16"
+    key = "scan_kernel<%s,%s,euler,gate,dskip> %s" % (io, io, w.name)
+    leg = {"workload": w.name, "batch": b, "d_inner": D, "seqlen": L, "d_state": N, "io": io, "segments": nseg,
+           "kernels": ("aggregate pass + carry + scan (one ssm_scan_fwd call)" if nseg > 1 else "scan"),
+           "launches": n, "ms_per_step": ms, "warm": pct(per), "elements_per_s": elems / (ms * 1e-3),
+           "hbm": hbm_roofline(nbytes, ms, measured_traffic(key), key),
+           "roofline": alu_roofline(slots, ms, key, measured_traffic(key))}
+    if log:
+        log("workload %s: %.4f ms per call (%d segments)" % (w.name, ms, nseg))
+    if cpu:
+        import oracle
+        oracle.build(force=False)
+        y32 = torch.empty((b, D, L), dtype=torch.float32, device=dev)
+        ssm.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dt_bias=d["dt_bias"], Dskip=d["Dskip"], z=d["z"],
+                     y=y32, h_final=hf, workspace=ws if ws_n else None, stream=stream)
+        torch.cuda.synchronize()
+        nch = LEG_CPU_CHANNELS.get(w.name)
+        sub = dict(host)
+        if nch is not None:   # the first nch channels of batch element 0
+            for k in ("x", "dt", "z"):
+                sub[k] = host[k][:1, :nch]
+            for k in ("B", "C"):
+                sub[k] = host[k][:1]
+            for k in ("A", "dt_bias", "Dskip"):
+                sub[k] = host[k][:nch]
+            yg = y32[:1, :nch].cpu().numpy().astype(np.float64)
+            hg = hf[:1, :nch].cpu().numpy().astype(np.float64)
+        else:
+            yg = y32.cpu().numpy().astype(np.float64)
+            hg = hf.cpu().numpy().astype(np.float64)
+        del y32
+        f = I.as_f64(sub)
+        cores = host_cores()
+        t0 = time.perf_counter()
+        yr, hr = oracle.scan(f["x"], f["dt"], f["A"], f["B"], f["C"], dt_bias=f["dt_bias"], Dskip=f["Dskip"],
+                             z=f["z"], nthreads=cores)
+        cs = time.perf_counter() - t0
+        ey = float(np.max(np.abs(yg - yr))) / float(np.sqrt(np.mean(yr * yr)))
+        eh = float(np.max(np.abs(hg - hr))) / float(np.sqrt(np.mean(hr * hr)))
+        tol = 1e-5 if w.io == I.F32 else 3e-3
+        leg["cpu_baseline"] = {"value": yr.size / cs, "unit": "elements/s", "cores": cores, "kind": "oracle",
+                               "seconds": cs,
+                               "sample": ("the whole workload" if nch is None else
+                                          "channels 0..%d of batch element 0, all %d steps" % (nch - 1, L)) + ", fp64"}
+        leg["parity_on_cpu_sample"] = {"max_abs_err_over_rms_y": ey, "h_final_err_over_rms": eh, "tolerance": tol,
+                                       "pass": bool(ey <= tol and eh <= tol), "elements": int(yr.size)}
+        if log:
+            log("workload %s: oracle %.2f s on %d cores, err y %.2e h %.2e" % (w.name, cs, cores, ey, eh))
+    return leg
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +401,11 @@ def main():
     ap.add_argument("--no-complex", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20)
+    ap.add_argument("--no-configs", action="store_true", help="skip the legs of the other scan workloads")
+    ap.add_argument("--workload", default=None,
+                    help="run only the forward scan of this workload (tiny-s6-fp32, mamba130m-layer, "
+                         "mamba2.8b-layer, million-length) for a few launches: for profiling")
+    ap.add_argument("--issue-rates-only", action="store_true", help="only run the issue-rate probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (torch) five times: the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -190,6 +423,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
@@ -199,6 +433,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read_per_launch": src.numel() * 4,
                           "copy_calibration_bytes_written_per_launch": dst.numel() * 4}), flush=True)
         return
+    if args.issue_rates_only:
+        print(json.dumps({"issue_rates": issue_rates(torch, dev, stream)}), flush=True)
+        return
 
     def up(a):
         if a is None:
@@ -207,8 +444,18 @@ def main():
             return torch.from_numpy(a).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
+    def log(msg):
+        print("bench: " + msg, file=sys.stderr, flush=True)
+
+    if args.workload:
+        w = next(w_ for w_ in I.WORKLOADS.values() if w_.name == args.workload and not w_.decode_steps)
+        leg = workload_leg(torch, np, ssm, I, up, w, dev, stream, steps=max(1, args.steps), cpu=False, log=log)
+        print(json.dumps({"workload_leg": leg}), flush=True)
+        return
+
     w = I.WORKLOADS[2]
     b, D, L, N = w.batch, w.dim, w.seqlen, w.dstate
+    log("headline workload %s: generating inputs" % w.name)
     host = I.scan_inputs(w)
     d = {k: up(v) for k, v in host.items()}
     y = torch.empty((b, D, L), dtype=torch.bfloat16, device=dev)
@@ -217,11 +464,18 @@ def main():
     nseg = ssm.plan_segments(p)
     ws_n = ssm.workspace_bytes(p)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+
+    from selective_state_space_57_amd import _abi
+    # arguments marshalled once: the binding's per-call checks take about as long as the kernel, so timing through
+    # it would measure the host (the GPU would idle between launches)
+    sargs = (d["x"].data_ptr(), d["dt"].data_ptr(), d["dt_bias"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
+             d["C"].data_ptr(), d["Dskip"].data_ptr(), d["z"].data_ptr(), 0, y.data_ptr(), hf.data_ptr(),
+             ws.data_ptr() if ws_n else 0, ws_n, stream.cuda_stream)
 
     def step():
-        ssm.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dt_bias=d["dt_bias"], Dskip=d["Dskip"], z=d["z"],
-                     y=y, h_final=hf, workspace=ws if ws_n else None, stream=stream)
+        st = _abi.scan_fwd_raw(p, *sargs)
+        if st:
+            _abi.check(st)
 
     for _ in range(args.warmup):
         step()
@@ -235,14 +489,17 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms = ev0.elapsed_time(ev1) / args.steps
+    # the same launches, each between two events: per-launch spread (a clock droop under sustained load shows as a
+    # rising median over p10)
+    _, per_launch = time_launches(torch, stream, step, max(10, args.steps))
+    log("headline: %.4f ms per step" % ms)
 
     elems = b * D * L
     value = elems / (ms * 1e-3)
     nbytes = scan_algorithmic_bytes(b, D, L, N)
-    flops = scan_algorithmic_flops(b, D, L, N)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    tflops = flops / (ms * 1e-3) / 1e12
+    slots = scan_algorithmic_slots(b, D, L, N)
     kernel_key = "scan_kernel<bf16,bf16,euler,gate,dskip> mamba2.8b-layer"
+    traffic = measured_traffic(kernel_key)
 
     out = {
         "metric": "scan elements/s (B*D*L), Mamba-2.8B-layer-shaped forward selective scan",
@@ -259,12 +516,18 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the Mamba-2.8B layer workload)",
         "config": {"workload": "mamba2.8b-layer", "batch": b, "d_inner": D, "seqlen": L, "d_state": N,
                    "io": "bf16", "state": "f32", "gate": True, "dskip": True, "disc": "euler-b", "segments": nseg},
-        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": gbs, "frac_of_8TBps": gbs / HBM_PEAK_GBS},
-        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / VALU_PEAK_TFLOPS, "traffic": measured_traffic(kernel_key),
-                     "kernel": kernel_key, "algorithmic_flops": flops},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "roofline": hbm_roofline(nbytes, ms, traffic, kernel_key)},
+        "roofline": alu_roofline(slots, ms, kernel_key, traffic,
+                                 {"hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "slots_per_element": scan_elem_slots(N)}),
+        "warm": dict(pct(per_launch), launches=len(per_launch),
+                     note="back-to-back launches, an event between consecutive ones"),
         "host_wall_ms_timed_region": wall_ms,
     }
+    log("issue-rate probe")
+    out["issue_rates"] = issue_rates(torch, dev, stream)
 
     # ---- context: what a plain device-to-device copy reaches here (1 GiB, read + written, timed after the scan)
     cp_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -279,7 +542,7 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * cp_src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     out["hbm"]["copy_ceiling_GBps"] = copy_gbs
-    out["hbm"]["frac_of_copy_ceiling"] = gbs / copy_gbs
+    out["hbm"]["frac_of_copy_ceiling"] = out["hbm"]["achieved_GBps"] / copy_gbs
     del cp_src, cp_dst
 
     # ---- context: single launches with the 256 MB Infinity Cache evicted before each (512 MB written by a fill
@@ -299,6 +562,15 @@ def main():
     out["cold"] = {"launches": len(cold), "median_ms": cold[len(cold) // 2], "p10_ms": cold[len(cold) // 10],
                    "p90_ms": cold[(9 * len(cold)) // 10], "elements_per_s_at_median": elems / (cold[len(cold) // 2] * 1e-3),
                    "flush": "512 MB written by a fill kernel before each launch"}
+
+    # ---- the other scan workloads (the tiny fp32 case, the 130M layer, the million-length sequence)
+    if not args.no_configs:
+        out["workloads"] = {}
+        for cfg in (0, 1, 3):
+            wk = I.WORKLOADS[cfg]
+            out["workloads"][wk.name] = workload_leg(torch, np, ssm, I, up, wk, dev, stream,
+                                                     cpu=not args.no_cpu_baseline, log=log)
+            torch.cuda.empty_cache()
 
     # ---- the same forward with the block's causal convolution (width 4) + SiLU fused in front of the scan
     if not args.no_conv:
@@ -325,11 +597,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / args.steps
-        cfl = flops + conv_algorithmic_flops(b, D, L, 4)
+        csl = slots + conv_algorithmic_slots(b, D, L, 4)
         out["conv_scan"] = {"workload": "mamba2.8b-layer + causal conv1d (width 4) + SiLU", "ms_per_step": cms,
                             "elements_per_s": elems / (cms * 1e-3), "overhead_vs_scan": cms / ms - 1.0,
-                            "algorithmic_flops": cfl, "achieved_TFLOPs": cfl / (cms * 1e-3) / 1e12,
-                            "frac_of_valu_peak": cfl / (cms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS,
+                            "roofline": alu_roofline(csl, cms, "scan_kernel<bf16,bf16,euler,gate,dskip,conv>"),
                             "algorithmic_bytes": nbytes + D * 4 * 5,
                             "note": "x is read once and the convolved sequence never goes to memory; a separate "
                                     "convolution kernel would add a write and a read of it (2 x 168 MB in bf16)"}
@@ -394,12 +665,11 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         xms = e0.elapsed_time(e1) / nx
-        xfl = complex_algorithmic_flops(b, D, L, N)
+        xsl = complex_algorithmic_slots(b, D, L, N)
         out["complex_scan"] = {"workload": "mamba2.8b-layer shape, complex diagonal A (S4D-Lin), complex B, C",
                                "ms_per_step": xms, "elements_per_s": elems / (xms * 1e-3),
-                               "ratio_to_real_scan": xms / ms, "algorithmic_flops": xfl,
-                               "achieved_TFLOPs": xfl / (xms * 1e-3) / 1e12,
-                               "frac_of_valu_peak": xfl / (xms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS}
+                               "ratio_to_real_scan": xms / ms,
+                               "roofline": alu_roofline(xsl, xms, "complex_scan_kernel mamba2.8b-layer")}
 
     # ---- Mamba-2 SSD layer (scalar A per head, N = 128) at the Mamba-2 2.7B layer shape, bf16 matrix cores
     if not args.no_ssd:
@@ -536,13 +806,12 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / args.bwd_steps
-        bfl = bwd_algorithmic_flops(b, D, L, N)
+        bsl = bwd_algorithmic_slots(b, D, L, N)
         bby = bwd_algorithmic_bytes(b, D, L, N)
         out["bwd"] = {"workload": "mamba2.8b-layer", "steps": args.bwd_steps, "ms_per_step": bms,
                       "elements_per_s": elems / (bms * 1e-3), "ratio_to_forward": bms / ms,
                       "kernels": "prep + carry + main + 2 reduce (one ssm_scan_bwd call)",
-                      "algorithmic_flops": bfl, "achieved_TFLOPs": bfl / (bms * 1e-3) / 1e12,
-                      "frac_of_valu_peak": bfl / (bms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS,
+                      "roofline": alu_roofline(bsl, bms, "ssm_scan_bwd (all five kernels)"),
                       "algorithmic_bytes": bby, "achieved_GBps": bby / (bms * 1e-3) / 1e9,
                       "workspace_bytes": wsb_n,
                       "main_kernel_traffic": measured_traffic("bwd_main_kernel<bf16,bf16,euler,gate> mamba2.8b-layer")}
@@ -582,12 +851,31 @@ def main():
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / wd.decode_steps
         dbytes = decode_algorithmic_bytes(wd.batch, wd.dim, wd.dstate)
+        dkey = "decode_kernel<bf16,bf16,euler,vec> decode-b256-d5120"
         out["decode"] = {"workload": "decode-b256-d5120", "steps": wd.decode_steps, "us_per_step": dms * 1e3,
                          "algorithmic_bytes_per_step": dbytes, "achieved_GBps": dbytes / (dms * 1e-3) / 1e9,
                          "frac_of_8TBps": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_kernel<bf16,bf16,euler,vec> decode-b256-d5120"),
+                         "roofline": hbm_roofline(dbytes, dms, measured_traffic(dkey), dkey),
+                         "traffic": measured_traffic(dkey),
                          "note": "64 consecutive steps, each with its own pre-generated x/dt/z/B/C tensors; the 84 MB "
                                  "fp32 state can be partly served by the 256 MB Infinity Cache"}
+        if not args.no_cpu_baseline:
+            import oracle
+            oracle.build(force=False)
+            st64 = I.decode_state(wd).astype(np.float64)
+            cs = []
+            for s_ in range(4):
+                f = I.as_f64(I.scan_inputs(wd, step=s_))
+                t0 = time.perf_counter()
+                _, st64 = oracle.state_update(st64, f["x"], f["dt"], f["A"], f["B"], f["C"], dt_bias=f["dt_bias"],
+                                              Dskip=f["Dskip"], z=f["z"], nthreads=host_cores())
+                cs.append(time.perf_counter() - t0)
+            cps = sorted(cs)[len(cs) // 2]
+            out["decode"]["cpu_baseline"] = {"value": cps * 1e6, "unit": "us/step", "cores": host_cores(),
+                                             "kind": "oracle", "seconds_per_step": cps,
+                                             "sample": "4 steps of the same workload (all 256 x 5120 channels), "
+                                                       "median, fp64"}
+        del state, steps_in
 
     # ---- CPU baseline: the fp64 oracle on the host cores over the same full step; also gates parity
     if not args.no_cpu_baseline:

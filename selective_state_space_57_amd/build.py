@@ -12,6 +12,9 @@ SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssm_scan.hip", "ssm_conv_scan.h
                                                   "ssm_scan_bwd.hip", "ssm_ssd.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm57.so")
+# the issue-rate probe that bench.py runs beside the scan (not part of the scan library's ABI)
+PROBE_SRC = os.path.join(HERE, "csrc", "issue_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libssm57_probe.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -33,20 +36,23 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every translation unit (in parallel) and link libssm57.so."""
+    """Compile every translation unit (in parallel), link libssm57.so, and build the issue-rate probe library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tag = ".tmp%d" % os.getpid()
     objs = [os.path.splitext(s)[0] + tag + ".o" for s in SRCS]
     try:
-        with ThreadPoolExecutor(len(SRCS)) as ex:
+        with ThreadPoolExecutor(len(SRCS) + 1) as ex:
+            probe = ex.submit(_run, [hipcc] + FLAGS + ["-shared", PROBE_SRC, "-o", PROBE_LIB + tag], verbose)
             list(ex.map(lambda so: _run([hipcc] + FLAGS + ["-I", INC, "-c", so[0], "-o", so[1]], verbose),
                         zip(SRCS, objs)))
+            probe.result()
         _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", LIB + tag], verbose)
     finally:
         for o in objs:
             if os.path.exists(o):
                 os.remove(o)
     os.replace(LIB + tag, LIB)
+    os.replace(PROBE_LIB + tag, PROBE_LIB)
     return LIB
 
 

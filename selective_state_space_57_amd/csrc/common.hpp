@@ -158,6 +158,15 @@ __device__ __forceinline__ void lds_write_b32(uint32_t lds_addr, float v) {
   asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(lds_addr), "v"(v), "i"(OFF) : "memory");
 }
 
+// two single-dword LDS writes in one instruction: v0 at lds_addr + 4 * OFF0, v1 at lds_addr + 4 * OFF1 (dword offsets
+// below 256)
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_write2_b32(uint32_t lds_addr, float v0, float v1) {
+  static_assert(OFF0 >= 0 && OFF0 < 256 && OFF1 >= 0 && OFF1 < 256, "ds_write2_b32 offsets are 8-bit dword counts");
+  asm volatile("ds_write2_b32 %0, %1, %2 offset0:%3 offset1:%4" : : "v"(lds_addr), "v"(v0), "v"(v1), "i"(OFF0),
+               "i"(OFF1) : "memory");
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -210,10 +210,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
         bq[4 * i + 3] = v.w;
       }
 
-      // ---- 16 sequential steps of the recurrence for this lane's state; each new state goes straight to LDS
-      // (single-dword writes: 64 lanes on 64 distinct banks) for the transposition below
+      // ---- 16 sequential steps of the recurrence for this lane's state; the new states of each pair of steps go to
+      // LDS with one two-dword write (one dword per step row: 64 lanes on 64 distinct banks per dword) for the
+      // transposition below.  LDS writes are the scarce resource here: a wave's single-dword write occupies the CU's
+      // LDS for about 4 cycles, a two-dword write about 6.
       if (!AGG) wave_lds_sync();  // the previous block's gathers of this row are done
       const uint32_t hw_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(hrow + n));
+      float hprev = 0.0f;
       static_for<kSub>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         const float dk = row_bcast<k>(delta);
@@ -227,7 +230,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
           bb = row_bcast<k>(dx) * bq[k];
         }
         h = fmaf(a, h, bb);
-        if (!AGG) lds_write_b32<k * kCtStride * 4>(hw_addr, h);
+        if constexpr (!AGG) {
+          if constexpr (k % 2 == 0) {
+            hprev = h;
+          } else if constexpr (k < 8) {  // dword offsets of the two writes must stay below 256
+            lds_write2_b32<(k - 1) * kCtStride, k * kCtStride>(hw_addr, hprev, h);
+          } else {
+            lds_write2_b32<(k - 9) * kCtStride, (k - 8) * kCtStride>(hw_addr + 8 * kCtStride * 4, hprev, h);
+          }
+        }
       });
 
       if (!AGG) {

@@ -11,23 +11,28 @@ pytestmark = pytest.mark.gpu
 
 
 def test_decode_workload_64_steps():
+    # 256 sequences x 5120 channels, 64 consecutive steps with fresh inputs: every output of every step and the
+    # state after every step against the oracle
     torch = G.torch_dev()
     w = I.WORKLOADS[4]
     st0 = I.decode_state(w)
     state = torch.from_numpy(st0.copy()).cuda()
-    sel = [0, 1, 137, w.batch - 1]                      # batches checked against the oracle (all 5120 channels)
-    ref_state = st0[sel].astype(np.float64)
+    ref_state = st0.astype(np.float64)
+    worst_y = worst_h = 0.0
     for s in range(w.decode_steps):
         d = I.scan_inputs(w, step=s)
         dd = G.to_dev(d)
         y = ssm.state_update(state, dd["x"], dd["dt"], dd["A"], dd["B"], dd["C"], dt_bias=dd["dt_bias"],
                              Dskip=dd["Dskip"], z=dd["z"], y_dtype=torch.float32)
         f = I.as_f64(d)
-        yr, ref_state = oracle.state_update(ref_state, f["x"][sel], f["dt"][sel], f["A"], f["B"][sel], f["C"][sel],
-                                            dt_bias=f["dt_bias"], Dskip=f["Dskip"], z=f["z"][sel])
-        yg = G.to_np64(y)[sel]
-        assert G.rel_max(yg, yr) <= G.TOL_BF16, ("step", s)
-    assert G.rel_max(G.to_np64(state)[sel], ref_state) <= G.TOL_BF16
+        yr, ref_state = oracle.state_update(ref_state, f["x"], f["dt"], f["A"], f["B"], f["C"],
+                                            dt_bias=f["dt_bias"], Dskip=f["Dskip"], z=f["z"])
+        ey = G.rel_max(G.to_np64(y), yr)
+        eh = G.rel_max(G.to_np64(state), ref_state)
+        worst_y, worst_h = max(worst_y, ey), max(worst_h, eh)
+        assert ey <= G.TOL_BF16, ("y at step", s, ey)
+        assert eh <= G.TOL_BF16, ("state after step", s, eh)
+    print("decode-b256-d5120: 64 steps, worst err y %.3e state %.3e (of rms)" % (worst_y, worst_h), flush=True)
 
 
 @pytest.mark.parametrize("io,disc,N", [("f32", 0, 16), ("f32", 1, 16), ("bf16", 0, 16), ("f32", 0, 5), ("bf16", 1, 1)])
