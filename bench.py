@@ -23,15 +23,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-# VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 3.93e13 lane-slots/s for non-packed fp32 (one add, multiply or
-# FMA per lane and slot; packed FP32 is not used).  Reported in units of 10^12 lane-slots/s.
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Issue cost of one v_exp_f32 / v_log_f32 / v_rcp_f32 in VALU slots.  The issue-rate probe
+# VALU issue: 256 CU x 4 SIMD x 32 lanes x 2.4 GHz = 7.86e13 lane-slots/s for non-packed fp32, where a slot is one
+# add, multiply or FMA per lane (a wave64 FMA issues every 2 cycles on gfx950; packed FP32 is not used).  This is the
+# published 157.3 TFLOP/s fp32 vector peak counted in FMAs.  Reported in units of 10^12 lane-slots/s.
+VALU_PEAK_TSLOTS = 256 * 4 * 32 * 2.4e9 / 1e12
+# Issue cost of one v_exp_f32 / v_log_f32 / v_rcp_f32 in slots.  The issue-rate probe
 # (selective_state_space_57_amd/csrc/issue_probe.hip, run by every bench.py call: `issue_rates` in the JSON line)
-# measures it on the box as (FMA rate) / (exp rate); on MI355X it reads 2.0-2.1, and an exp interleaved with FMAs in
-# one wave, or issued by another wave of the same SIMD, costs the same two slots (no co-issue).  The record is in
+# measures on MI355X about 2.4 cycles per wave64 FMA and 8.2 per wave64 exp, and an exp interleaved with FMAs in one
+# wave, or issued by another wave of the same SIMD, costs the same (no co-issue): 4 slots.  The record is in
 # profiles/issue_rates_mi355x.md.
-TRANS_SLOTS = 2
+TRANS_SLOTS = 4
 
 
 def scan_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
@@ -42,14 +43,15 @@ def scan_algorithmic_bytes(b, D, L, N, io_bytes=2, gate=True, dskip=True):
     return seq + bc + par + b * D * N * 4
 
 
-SOFTPLUS_SLOTS = 13   # -|u| log2(e), exp (2), 1 + v, w - 1, v - (w - 1), 1 - v, log2 (2), x ln 2, fma, max(u, 0), +
-SILU_SLOTS = 7        # -z log2(e), exp (2), 1 + e, rcp (2), z r
+# -|u| log2(e), exp, 1 + v, w - 1, v - (w - 1), 1 - v, log2, x ln 2, fma, max(u, 0), +
+SOFTPLUS_SLOTS = 9 + 2 * TRANS_SLOTS
+SILU_SLOTS = 3 + 2 * TRANS_SLOTS      # -z log2(e), exp, 1 + e, rcp, z r
 
 
 def scan_elem_slots(N, gate=True, dskip=True, softplus=True):
     """Algorithmic VALU issue slots of the forward scan per (b, d, t) element (transcendental = TRANS_SLOTS).
-    Per state n: Delta*A' (1), exp (2), (Delta x)*B (1), h = a h + b (1 FMA), y += C h (1 FMA)  -> 6;
-    per element: dt + bias (1), softplus (13), Delta*x (1), D*x (1 FMA), silu (7) and the gate's product (1)."""
+    Per state n: Delta*A' (1), exp (TRANS_SLOTS), (Delta x)*B (1), h = a h + b (1 FMA), y += C h (1 FMA);
+    per element: dt + bias (1), softplus, Delta*x (1), D*x (1 FMA), silu and the gate's product (1)."""
     per_elem = 1 + (SOFTPLUS_SLOTS if softplus else 0) + 1 + (1 if dskip else 0) + (SILU_SLOTS + 1 if gate else 0)
     return (4 + TRANS_SLOTS) * N + per_elem
 
@@ -59,9 +61,10 @@ def scan_algorithmic_slots(b, D, L, N, gate=True, dskip=True, softplus=True):
 
 
 def complex_algorithmic_slots(b, D, L, N, gate=True, dskip=True):
-    """Complex-A forward per (b, d, t): per state Delta*Re(A), exp (2), sin + cos (4), (Delta x) B (2), the complex
-    update (4), Re(C h) (2) and its sum (1) = 16; per element as the real scan."""
-    return float(16 * N + scan_elem_slots(0, gate, dskip)) * b * D * L
+    """Complex-A forward per (b, d, t): per state Delta*Re(A), exp, sin + cos (about 18 fused multiply-adds and bit
+    operations of the polynomial evaluation with its reduction), (Delta x) B (2), the complex update (4), Re(C h) (2)
+    and its sum (1); per element as the real scan."""
+    return float((1 + TRANS_SLOTS + 18 + 2 + 4 + 2 + 1) * N + scan_elem_slots(0, gate, dskip)) * b * D * L
 
 
 def conv_algorithmic_slots(b, D, L, width=4):
@@ -71,12 +74,13 @@ def conv_algorithmic_slots(b, D, L, width=4):
 
 def bwd_algorithmic_slots(b, D, L, N, gate=True, dskip=True):
     """VALU issue slots of the backward per (b, d, t) (same convention as the forward).
-    Per state n: zero-start chunk pass 8 (Delta*A, exp 2, (Delta x)*B, h FMA, decay product, C*ds, lambda FMA);
-    recomputation 5 (Delta*A, exp 2, (Delta x)*B, h FMA); adjoint 2 (g += C ds, g *= a); dA 3 (a h_prev, g u,
+    Per state n: zero-start chunk pass (Delta*A, exp, (Delta x)*B, h FMA, decay product, C*ds, lambda FMA);
+    recomputation (Delta*A, exp, (Delta x)*B, h FMA); adjoint 2 (g += C ds, g *= a); dA 3 (a h_prev, g u,
     += Delta); dx / dDelta terms 2 (g B, A g u) and their sums over n 2; dB / dC 2 FMA; with the gate C h and its sum 2.
-    Per element: softplus twice (13 each), sigmoid(u) 4, silu twice (7 each), dz 4, dx / dDelta / du 4."""
-    per_n = 8 + 5 + 2 + 3 + 4 + 2 + (2 if gate else 0)
-    per_elem = SOFTPLUS_SLOTS * 2 + 4 + (SILU_SLOTS * 2 + 4 if gate else 0) + 4 + (2 if dskip else 0)
+    Per element: softplus twice, sigmoid(u) (exp, add, rcp), silu twice, dz 4, dx / dDelta / du 4."""
+    per_n = (6 + TRANS_SLOTS) + (3 + TRANS_SLOTS) + 2 + 3 + 4 + 2 + (2 if gate else 0)
+    per_elem = (SOFTPLUS_SLOTS * 2 + 1 + 2 * TRANS_SLOTS + (SILU_SLOTS * 2 + 4 if gate else 0) + 4
+                + (2 if dskip else 0))
     return float(per_n * N + per_elem) * b * D * L
 
 
@@ -85,8 +89,9 @@ def alu_roofline(slots, ms, kernel, traffic=None, extra=None):
     ach = slots / (ms * 1e-3) / 1e12
     r = {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_TSLOTS, "unit": "Tslot/s", "frac": ach / VALU_PEAK_TSLOTS,
          "traffic": traffic, "kernel": kernel, "algorithmic_slots": slots,
-         "slot_model": "one fp32 add / multiply / FMA per lane = 1 slot, one exp / log / rcp = %d slots; peak = 256 CU "
-                       "x 4 SIMD x 16 lanes x 2.4 GHz (non-packed fp32)" % TRANS_SLOTS}
+         "slot_model": "one fp32 add / multiply / FMA per lane = 1 slot, one exp / log / rcp = %d slots (measured "
+                       "in issue_rates); peak = 256 CU x 4 SIMD x 32 lanes x 2.4 GHz (non-packed fp32; the 157.3 "
+                       "TFLOP/s fp32 vector peak in FMAs)" % TRANS_SLOTS}
     if extra:
         r.update(extra)
     return r

@@ -29,10 +29,17 @@ struct ScanArgs {
   const float* h0;
   void* y;
   float* h_final;
-  float* ws_h;    // [nseg][batch*dim][N]: segment end states (first pass), then carry-in states
-  float* ws_sum;  // [nseg][batch*dim]: per-segment sum of Delta
   int64_t batch, dim, L, seg_len;
   int N, nseg, softplus;
+  // L-segments (nseg > 1): per segment s and channel ch, with `win` the length of each segment's correction window
+  float* ws_e;     // [nseg][bd][N]: state at the segment's end (segment 0 from h0, the others from zero)
+  float* ws_hw;    // [nseg][bd][N]: zero-start state after the first `win` steps (segments with more steps)
+  float* ws_hin;   // [nseg][bd][N]: true state entering the segment (written by carry_kernel)
+  float* ws_sum;   // [nseg][bd]: sum of Delta over the segment
+  float* ws_sumw;  // [nseg][bd]: sum of Delta over the first `win` steps
+  int* ws_flag;    // [nseg][bd]: 1 = the carry-in still matters after `win` steps, so the rest is rescanned
+  float* ws_y0;    // [nseg][bd][win]: zero-start pre-gate outputs of the first `win` steps
+  int win;
   // causal convolution in front of the scan (CONV kernels only)
   const float* conv_w;      // [dim][conv_k]
   const float* conv_b;      // [dim] or null
@@ -40,26 +47,42 @@ struct ScanArgs {
   int conv_k, conv_silu;
 };
 
+// How a launch of scan_kernel covers the sequence.
+//   kWhole:   one segment, from h0 to h_final.
+//   kSegMain: every L-segment at once, segment 0 from h0 and the others from zero.  In segments s >= 1 the first
+//             `win` steps store their pre-gate outputs to ws_y0 instead of y (they still lack the carry-in's part);
+//             the segment's end state, sum of Delta and the state and Delta sum after `win` steps go to the workspace.
+//   kSegCorr: segments s >= 1 after carry_kernel: the carry-in's part of the first `win` steps, and, where it has
+//             not yet decayed below the state's rounding (ws_flag), a rescan of the rest of the segment.
+// The state is linear in the carry-in h_in: h_t = h0_t + (prod_{r<=t} Abar_r) h_in, so its part of y_t is
+// sum_n C_n(t) g_n(t) with g_t = Abar_t g_{t-1}, g = h_in at the segment start (the tutorial's associative combine
+// (a1, b1) o (a2, b2) = (a2 a1, a2 b1 + b2) applied at the segment boundary).  It decays with the state's memory, so
+// only a window of each segment needs it; carry_kernel checks that per channel.
+enum ScanMode : int { kWhole = 0, kSegMain = 1, kSegCorr = 2 };
+// what a 64-step chunk does
+enum ChunkPhase : int { kFullInput = 0, kWindowOut = 1, kHomog = 2 };
+// steps of each segment whose outputs the correction pass completes (a multiple of the 64-step chunk)
+constexpr int kCorrWindow = 2048;
+
 // ---------------------------------------------------------------------------------------------------------------
-// The scan kernel.  AGG = true: first pass of the segmented scan (zero start, no output; writes the end state and
-// the sum of Delta of each segment).  AGG = false: the fused forward scan of one segment (or the whole sequence).
+// The scan kernel (see ScanMode for the segment passes).
 //
 // Per 64-step chunk a lane owns four steps of its channel (t0 + 16 s + n, s = 0..3) for loading x, dt, z, computing
 // Delta and Delta*x, contracting with C and storing y, plus four B and four C values it stages into LDS.  All of
 // these global loads are issued one chunk ahead, so their latency hides behind a whole chunk of arithmetic.
-template <typename TI, typename TY, bool ZOH, bool AGG, bool GATE, bool DSKIP, bool CONV>
+template <typename TI, typename TY, bool ZOH, int MODE, bool GATE, bool DSKIP, bool CONV>
 // five resident workgroups per CU (<= 96 VGPRs): a 4 x 5120-channel layer is exactly 5 workgroups per CU
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void scan_kernel(ScanArgs p) {
-  __shared__ __align__(16) float sB[kChanPerWG][kBStride];           // B_n(t) of the chunk, [n][t]
-  __shared__ __align__(16) float sCt[AGG ? 1 : kChunk][kCtStride];   // C_n(t) of the chunk, [t][n]
-  __shared__ __align__(16) float sH[AGG ? 1 : kChanPerWG * kHRow];   // states of a 16-step block, per row [t][n]
+  __shared__ __align__(16) float sB[kChanPerWG][kBStride];     // B_n(t) of the chunk, [n][t]
+  __shared__ __align__(16) float sCt[kChunk][kCtStride];       // C_n(t) of the chunk, [t][n]
+  __shared__ __align__(16) float sH[kChanPerWG * kHRow];       // states of a 16-step block, per row [t][n]
 
   const int tid = threadIdx.x;
   const int n = tid & 15;    // state index of this lane; also the step index it owns within a 16-step block
   const int row = tid >> 4;  // channel within the workgroup
   const int64_t d = static_cast<int64_t>(blockIdx.x) * kChanPerWG + row;
   const int64_t b = blockIdx.y;
-  const int seg = blockIdx.z;
+  const int seg = MODE == kSegCorr ? static_cast<int>(blockIdx.z) + 1 : static_cast<int>(blockIdx.z);
   const bool chv = d < p.dim;
   const bool nv = n < p.N;
   const int64_t ch = b * p.dim + d;
@@ -67,6 +90,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   const int ts = seg * static_cast<int>(p.seg_len);
   const int te = ts + static_cast<int>(p.seg_len) < L ? ts + static_cast<int>(p.seg_len) : L;
   const int64_t bdN = p.batch * p.dim;
+  // end of the correction window (segments s >= 1 of the segmented passes)
+  const int tw = (MODE != kWhole && seg > 0) ? (ts + p.win < te ? ts + p.win : te) : ts;
 
   // descriptors start at the workgroup's first channel row (x, dt, z, y) and at the batch's B / C rows
   const int64_t row0 = b * p.dim + static_cast<int64_t>(blockIdx.x) * kChanPerWG;
@@ -75,8 +100,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   const auto rd_ = make_rsrc(static_cast<const TI*>(p.dt) + row0 * p.L, rows_left * p.L);
   const auto rz_ = make_rsrc(GATE ? static_cast<const TI*>(p.z) + row0 * p.L : static_cast<const TI*>(p.x),
                              GATE ? rows_left * p.L : 0);
-  const auto ry_ = make_rsrc(AGG ? static_cast<const TY*>(nullptr) : static_cast<const TY*>(p.y) + row0 * p.L,
-                             AGG ? 0 : rows_left * p.L);
+  const auto ry_ = make_rsrc(static_cast<const TY*>(p.y) + row0 * p.L, rows_left * p.L);
   const auto rb_ = make_rsrc(static_cast<const TI*>(p.B) + b * p.N * p.L, static_cast<int64_t>(p.N) * p.L);
   const auto rc_ = make_rsrc(static_cast<const TI*>(p.C) + b * p.N * p.L, static_cast<int64_t>(p.N) * p.L);
   const int nn = tid >> 4, q = tid & 15;  // staging role: B/C of state nn at steps 4q .. 4q+3 of the chunk
@@ -88,6 +112,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   // C staging role: step ct of the chunk, states 4 cg .. 4 cg + 3 (consecutive lanes write consecutive LDS rows)
   const int ct = tid & 63, cg = tid >> 6;
   const uint32_t lane_co = (static_cast<uint32_t>(4 * cg) * static_cast<uint32_t>(L) + ct) * SI;
+  // this lane's row of the pre-gate window outputs (segmented passes; index by t - ts)
+  float* const y0row = (MODE != kWhole && chv) ? p.ws_y0 + (static_cast<int64_t>(seg) * bdN + ch) * p.win : nullptr;
 
   const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
   const float Ap = An * kLog2e;                                   // exp(Delta*A) = exp2(Delta*A*log2(e))
@@ -98,28 +124,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   // CONV: taps of this row's channel right-aligned in cw[0..3] (missing taps 0), and xprev = the input at this lane's
   // step of the previous 16-step block: lanes 13..15 of it supply steps t-3..t-1 to the first lanes of the next block
   float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, xprev = 0.0f;
+  auto load_xprev = [&](int t_start) {  // the inputs before t_start: the sequence itself, or the incoming window
+    if constexpr (CONV) {
+      if (chv) {
+        const int K = p.conv_k;
+        const int tau = t_start - kSub + n;
+        xprev = 0.0f;
+        if (tau >= 0)
+          xprev = Elem<TI>::ld(static_cast<const TI*>(p.x), ch * p.L + tau);
+        else if (p.conv_state && tau >= -(K - 1))
+          xprev = p.conv_state[ch * (K - 1) + (K - 1) + tau];
+      }
+    }
+  };
   if constexpr (CONV) {
     if (chv) {
       const int K = p.conv_k;
       for (int k = 0; k < K; ++k) cw[4 - K + k] = p.conv_w[d * K + k];
       cb = p.conv_b ? p.conv_b[d] : 0.0f;
-      const int tau = ts - kSub + n;  // before the segment: the sequence itself, or the state before step 0
-      if (tau >= 0)
-        xprev = Elem<TI>::ld(static_cast<const TI*>(p.x), ch * p.L + tau);
-      else if (p.conv_state && tau >= -(K - 1))
-        xprev = p.conv_state[ch * (K - 1) + (K - 1) + tau];
     }
+    load_xprev(MODE == kSegCorr ? tw : ts);
   }
 
   float h = 0.0f;
-  if (!AGG && chv && nv) {
-    if (p.nseg > 1)
-      h = p.ws_h[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n];
-    else if (p.h0)
+  if (chv && nv) {
+    if (MODE == kSegCorr)
+      h = p.ws_hin[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n];
+    else if (seg == 0 && p.h0)
       h = p.h0[ch * p.N + n];
   }
-  float dsum = 0.0f;  // AGG: this lane's share of the segment's sum of Delta
-  float* const hrow = AGG ? nullptr : &sH[row * kHRow];
+  // the correction pass continues past its window only where some channel of the workgroup needs it
+  bool rescan = false;
+  if constexpr (MODE == kSegCorr) rescan = __syncthreads_or(chv && n == 0 && tw < te && p.ws_flag[seg * bdN + ch]) != 0;
+  const int tend = (MODE == kSegCorr && !rescan) ? tw : te;
+  float dsum = 0.0f;  // segmented main pass: this lane's share of the sum of Delta
+  float* const hrow = &sH[row * kHRow];
 
   // raw (unconverted) prefetch registers for one chunk.  Reads past the tensors return 0; reads past the segment
   // or the row are masked off below.
@@ -138,16 +177,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       rb[k] = Buf<TI>::ld(rb_, bo + k * SI);
-      if (!AGG) rc[k] = Buf<TI>::ld(rc_, co + static_cast<uint32_t>(k) * static_cast<uint32_t>(L) * SI);
+      rc[k] = Buf<TI>::ld(rc_, co + static_cast<uint32_t>(k) * static_cast<uint32_t>(L) * SI);
     }
   };
   // zero a value unless `ok` (bitwise, so that whatever was read at a clamped index cannot leak in)
   auto keep = [](bool ok, float v) { return __int_as_float(__float_as_int(v) & (ok ? -1 : 0)); };
+  // sum of a value over the 16 lanes of each row (every lane receives it)
+  auto row_sum = [](float v) {
+    v += __shfl_xor(v, 8, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 1, 16);
+    return v;
+  };
 
   const bool wg_full = static_cast<int64_t>(blockIdx.x) * kChanPerWG + kChanPerWG <= p.dim && p.N == kSub;
 
-  // one 64-step chunk; FULL: every step and every channel / state of the workgroup is valid, so no masking
-  auto chunk = [&]<bool FULL>(int t0) {
+  // one 64-step chunk; FULL: every step and every channel / state of the workgroup is valid, so no masking.
+  // PH = kFullInput: the scan as defined; kWindowOut: the same, but the pre-gate output goes to ws_y0; kHomog: no
+  // input (the carry-in's part), y = (ws_y0 + sum_n C_n h_n) silu(z)
+  auto chunk = [&]<bool FULL, int PH>(int t0) {
     // ---- stage the prefetched B and C of this chunk (zero outside the sequence / state range)
     float bv[4], cv[4];
 #pragma unroll
@@ -155,13 +204,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       const bool okb = FULL || (nnv && (t0 + 4 * q + k) < te);
       const bool okc = FULL || ((4 * cg + k) < p.N && (t0 + ct) < te);
       bv[k] = keep(okb, Buf<TI>::cvt(rb[k]));
-      cv[k] = AGG ? 0.0f : keep(okc, Buf<TI>::cvt(rc[k]));
+      cv[k] = keep(okc, Buf<TI>::cvt(rc[k]));
     }
     __syncthreads();  // the previous chunk's readers of sB / sCt are done
-    *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
-    if (!AGG) *reinterpret_cast<float4*>(&sCt[ct][4 * cg]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+    if constexpr (PH != kHomog) *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+    *reinterpret_cast<float4*>(&sCt[ct][4 * cg]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
     __syncthreads();
-    const bool more = t0 + kChunk < te;  // uniform
+    const bool more = t0 + kChunk < tend;  // uniform
     if (more) fetch_staged(t0 + kChunk);
 
 #pragma unroll
@@ -171,8 +220,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       const int t = tb + n;
       const bool ev = FULL || (chv && t < te);
       // ---- this lane's owned step: convert it, then reuse its ring slot for the block two ahead
-      float xv;
-      if constexpr (CONV) {  // u_t = act(b + w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3})
+      float xv = 0.0f;
+      if constexpr (PH == kHomog) {
+        // no input in the correction window
+      } else if constexpr (CONV) {  // u_t = act(b + w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3})
         const float xin = Buf<TI>::cvt(rx[s & 1]);
         // both rotations first, with every lane active (a DPP read from a lane switched off by a branch yields 0),
         // then the per-lane choice
@@ -193,70 +244,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       }
       const float uv = keep(ev, Buf<TI>::cvt(rd[s & 1]) + bias);
       const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s & 1])) : 0.0f;
-      if (tb + 2 * kSub < te) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
+      if (tb + 2 * kSub < tend) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
       float delta = p.softplus ? softplus(uv) : uv;
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
-      if (AGG) dsum += delta;
+      if (MODE == kSegMain) dsum += delta;
 
       // ---- B_n(tb .. tb+15) from LDS
       float bq[kSub];
+      if constexpr (PH != kHomog) {
 #pragma unroll
-      for (int i = 0; i < kSub / 4; ++i) {
-        const float4 v = *reinterpret_cast<const float4*>(&sB[n][s * kSub + 4 * i]);
-        bq[4 * i + 0] = v.x;
-        bq[4 * i + 1] = v.y;
-        bq[4 * i + 2] = v.z;
-        bq[4 * i + 3] = v.w;
+        for (int i = 0; i < kSub / 4; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(&sB[n][s * kSub + 4 * i]);
+          bq[4 * i + 0] = v.x;
+          bq[4 * i + 1] = v.y;
+          bq[4 * i + 2] = v.z;
+          bq[4 * i + 3] = v.w;
+        }
       }
 
       // ---- 16 sequential steps of the recurrence for this lane's state; the new states of each pair of steps go to
       // LDS with one two-dword write (one dword per step row: 64 lanes on 64 distinct banks per dword) for the
       // transposition below.  LDS writes are the scarce resource here: a wave's single-dword write occupies the CU's
       // LDS for about 4 cycles, a two-dword write about 6.
-      if (!AGG) wave_lds_sync();  // the previous block's gathers of this row are done
+      wave_lds_sync();  // the previous block's gathers of this row are done
       const uint32_t hw_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(hrow + n));
       float hprev = 0.0f;
       static_for<kSub>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         const float dk = row_bcast<k>(delta);
         const float a = hw_exp2(dk * Ap);
-        float bb;
-        if (ZOH) {
-          const float en = dk * An;
-          const float coef = An != 0.0f ? expm1_from(en, a) * rA : dk;
-          bb = coef * bq[k] * row_bcast<k>(xv);
+        if constexpr (PH == kHomog) {
+          h = a * h;
         } else {
-          bb = row_bcast<k>(dx) * bq[k];
-        }
-        h = fmaf(a, h, bb);
-        if constexpr (!AGG) {
-          if constexpr (k % 2 == 0) {
-            hprev = h;
-          } else if constexpr (k < 8) {  // dword offsets of the two writes must stay below 256
-            lds_write2_b32<(k - 1) * kCtStride, k * kCtStride>(hw_addr, hprev, h);
+          float bb;
+          if (ZOH) {
+            const float en = dk * An;
+            const float coef = An != 0.0f ? expm1_from(en, a) * rA : dk;
+            bb = coef * bq[k] * row_bcast<k>(xv);
           } else {
-            lds_write2_b32<(k - 9) * kCtStride, (k - 8) * kCtStride>(hw_addr + 8 * kCtStride * 4, hprev, h);
+            bb = row_bcast<k>(dx) * bq[k];
           }
+          h = fmaf(a, h, bb);
+        }
+        if constexpr (k % 2 == 0) {
+          hprev = h;
+        } else if constexpr (k < 8) {  // dword offsets of the two writes must stay below 256
+          lds_write2_b32<(k - 1) * kCtStride, k * kCtStride>(hw_addr, hprev, h);
+        } else {
+          lds_write2_b32<(k - 9) * kCtStride, (k - 8) * kCtStride>(hw_addr + 8 * kCtStride * 4, hprev, h);
         }
       });
 
-      if (!AGG) {
-        // ---- transpose through LDS: lane j of the row gathers h_n(tb + j) for all n and contracts with C
-        wave_lds_sync();
-        float acc = 0.0f;
-        const float* hs = &hrow[n * kCtStride];
-        const float* cs = &sCt[s * kSub + n][0];
+      // ---- transpose through LDS: lane j of the row gathers h_n(tb + j) for all n and contracts with C
+      wave_lds_sync();
+      float acc = 0.0f;
+      const float* hs = &hrow[n * kCtStride];
+      const float* cs = &sCt[s * kSub + n][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 hh = *reinterpret_cast<const float4*>(hs + 4 * i);
-          const float4 cc = *reinterpret_cast<const float4*>(cs + 4 * i);
-          acc = fmaf(cc.x, hh.x, acc);
-          acc = fmaf(cc.y, hh.y, acc);
-          acc = fmaf(cc.z, hh.z, acc);
-          acc = fmaf(cc.w, hh.w, acc);
-        }
-        if (DSKIP) acc = fmaf(Dv, xv, acc);
+      for (int i = 0; i < 4; ++i) {
+        const float4 hh = *reinterpret_cast<const float4*>(hs + 4 * i);
+        const float4 cc = *reinterpret_cast<const float4*>(cs + 4 * i);
+        acc = fmaf(cc.x, hh.x, acc);
+        acc = fmaf(cc.y, hh.y, acc);
+        acc = fmaf(cc.z, hh.z, acc);
+        acc = fmaf(cc.w, hh.w, acc);
+      }
+      if constexpr (PH == kHomog) {
+        if (ev) acc += y0row[t - ts];  // the zero-start part (with D x) from the main pass
+      } else if (DSKIP) {
+        acc = fmaf(Dv, xv, acc);
+      }
+      if constexpr (PH == kWindowOut) {
+        if (ev) y0row[t - ts] = acc;  // pre-gate: completed by the correction pass
+      } else {
         if (GATE) acc *= silu(zv);
         // out-of-range offset for steps outside the segment: the hardware drops the write
         Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
@@ -266,46 +327,95 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
 
   fetch_staged(ts);
   fetch_owned(ts, 0);
-  if (ts + kSub < te) fetch_owned(ts + kSub, 1);
-  for (int t0 = ts; t0 < te; t0 += kChunk) {
-    if (wg_full && t0 + kChunk <= te)
-      chunk.template operator()<true>(t0);
-    else
-      chunk.template operator()<false>(t0);
+  if (ts + kSub < tend) fetch_owned(ts + kSub, 1);
+  for (int t0 = ts; t0 < tend; t0 += kChunk) {
+    const bool full = wg_full && t0 + kChunk <= te;
+    if (MODE != kWhole && t0 < tw) {  // the correction window of segments s >= 1 (uniform)
+      if constexpr (MODE == kSegCorr) {
+        if (full) chunk.template operator()<true, kHomog>(t0);
+        else chunk.template operator()<false, kHomog>(t0);
+      } else {
+        if (full) chunk.template operator()<true, kWindowOut>(t0);
+        else chunk.template operator()<false, kWindowOut>(t0);
+      }
+      if (t0 + kChunk == tw && tw < te) {  // the window ends inside the segment
+        const int64_t o = (static_cast<int64_t>(seg) * bdN + ch) * p.N + n;
+        if constexpr (MODE == kSegMain) {
+          if (chv && nv) p.ws_hw[o] = h;
+          const float sw = row_sum(dsum);
+          if (chv && n == 0) p.ws_sumw[seg * bdN + ch] = sw;
+        } else {  // rescan from the true state: the zero-start state plus the carry-in's part
+          if (chv && nv) h += p.ws_hw[o];
+          if constexpr (CONV) load_xprev(tw);
+        }
+      }
+    } else {
+      if (full) chunk.template operator()<true, kFullInput>(t0);
+      else chunk.template operator()<false, kFullInput>(t0);
+    }
   }
 
-  if (AGG) {
-    if (chv && nv) p.ws_h[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n] = h;
-    // sum of Delta over the row's 16 owners
-    dsum += __shfl_xor(dsum, 8, 16);
-    dsum += __shfl_xor(dsum, 4, 16);
-    dsum += __shfl_xor(dsum, 2, 16);
-    dsum += __shfl_xor(dsum, 1, 16);
-    if (chv && n == 0) p.ws_sum[static_cast<int64_t>(seg) * bdN + ch] = dsum;
-  } else {
-    if (p.h_final && chv && nv && seg == p.nseg - 1) p.h_final[ch * p.N + n] = h;
+  if constexpr (MODE == kWhole) {
+    if (p.h_final && chv && nv) p.h_final[ch * p.N + n] = h;
+  } else if constexpr (MODE == kSegMain) {
+    if (chv && nv) p.ws_e[(static_cast<int64_t>(seg) * bdN + ch) * p.N + n] = h;
+    const float st = row_sum(dsum);
+    if (chv && n == 0) p.ws_sum[seg * bdN + ch] = st;
   }
 }
 
-// Chains the segment aggregates into carry-in states: h_in[0] = h0, h_in[s+1] = exp(A * sum_s Delta) h_in[s] + e_s,
-// where e_s is segment s's end state from a zero start (the associative combine of the tutorial's parallel scan).
-__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A, const float* __restrict__ h0,
-                                                    float* __restrict__ ws_h, const float* __restrict__ ws_sum,
-                                                    int64_t batch, int64_t dim, int N, int nseg) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t bdN = batch * dim;
-  if (i >= bdN * N) return;
-  const int64_t ch = i / N;
-  const int n = static_cast<int>(i % N);
-  const int64_t d = ch % dim;
-  const float Ap = A[d * N + n] * kLog2e;
-  float run = h0 ? h0[i] : 0.0f;
-  for (int s = 0; s < nseg; ++s) {
-    const int64_t k = static_cast<int64_t>(s) * bdN * N + i;
-    const float e = (s < nseg - 1) ? ws_h[k] : 0.0f;
-    const float sum = (s < nseg - 1) ? ws_sum[static_cast<int64_t>(s) * bdN + ch] : 0.0f;
-    ws_h[k] = run;
-    run = fmaf(hw_exp2(sum * Ap), run, e);
+// Chains the segments, one thread per channel: h_in[1] = the state at segment 0's end; h_in[s+1] =
+// exp(A * sum_s Delta) h_in[s] + e_s, with e_s segment s's end state from zero (exp(A sum Delta) is the product of
+// the segment's decays); the last one is h_final.  Also decides, per segment s >= 1 with more than `win` steps,
+// whether the carry-in still matters after the window: its part of the state there, |exp(A sum_w Delta) h_in|,
+// summed over n, above 2^-24 of the zero-start state's (so that it could still change a rounded state), or a
+// non-negative A (no decay).
+__global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t bdN = p.batch * p.dim;
+  if (ch >= bdN) return;
+  const int64_t d = ch % p.dim;
+  const int N = p.N;
+  float h[kSub], ap[kSub];
+  bool grows = false;
+#pragma unroll
+  for (int n = 0; n < kSub; ++n) {
+    const float a = n < N ? p.A[d * N + n] : -1.0f;
+    grows = grows || a >= 0.0f;
+    ap[n] = a * kLog2e;
+    h[n] = n < N ? p.ws_e[ch * N + n] : 0.0f;
+  }
+  for (int s = 1; s < p.nseg; ++s) {
+    const int64_t o = (static_cast<int64_t>(s) * bdN + ch) * N;
+    const int64_t ts = static_cast<int64_t>(s) * p.seg_len;
+    const int64_t te = ts + p.seg_len < p.L ? ts + p.seg_len : p.L;
+    int flag = 0;
+    if (te - ts > p.win) {
+      const float sw = p.ws_sumw[s * bdN + ch];
+      float cor = 0.0f, ref = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kSub; ++n) {
+        if (n < N) {
+          cor += fabsf(hw_exp2(sw * ap[n]) * h[n]);
+          ref += fabsf(p.ws_hw[o + n]);
+        }
+      }
+      flag = (grows || cor > 0x1p-24f * ref) ? 1 : 0;
+    }
+    p.ws_flag[s * bdN + ch] = flag;
+    const float sum = p.ws_sum[s * bdN + ch];
+#pragma unroll
+    for (int n = 0; n < kSub; ++n) {
+      if (n < N) {
+        p.ws_hin[o + n] = h[n];
+        h[n] = fmaf(hw_exp2(sum * ap[n]), h[n], p.ws_e[o + n]);
+      }
+    }
+  }
+  if (p.h_final) {
+#pragma unroll
+    for (int n = 0; n < kSub; ++n)
+      if (n < N) p.h_final[ch * N + n] = h[n];
   }
 }
 
@@ -481,11 +591,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 struct Plan {
   int nseg;
   int64_t seg_len;
+  int win;  // correction window of segments s >= 1 (nseg > 1)
   size_t ws_bytes;
 };
 
+// byte offsets of the segmented scan's workspace arrays (see ScanArgs), each 256-byte aligned
+struct SegLayout {
+  size_t e, hw, hin, sum, sumw, flag, y0, total;
+};
+
+inline SegLayout seg_layout(int64_t nseg, int64_t bd, int64_t N, int64_t win) {
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  SegLayout l{};
+  const size_t states = static_cast<size_t>(nseg * bd * N) * sizeof(float);
+  const size_t per_ch = static_cast<size_t>(nseg * bd) * sizeof(float);
+  l.e = 0;
+  l.hw = l.e + up(states);
+  l.hin = l.hw + up(states);
+  l.sum = l.hin + up(states);
+  l.sumw = l.sum + up(per_ch);
+  l.flag = l.sumw + up(per_ch);
+  l.y0 = l.flag + up(per_ch);
+  l.total = l.y0 + up(static_cast<size_t>(nseg * bd) * static_cast<size_t>(win) * sizeof(float));
+  return l;
+}
+
 Plan make_plan(const ssm_scan_params* p) {
-  Plan pl{1, p->seqlen, 0};
+  Plan pl{1, p->seqlen, 0, 0};
   const int64_t chunks = (p->seqlen + kChunk - 1) / kChunk;
   int64_t nseg = 1;
   if (p->segments > 0) {
@@ -506,43 +638,42 @@ Plan make_plan(const ssm_scan_params* p) {
   pl.seg_len = seg_chunks * kChunk;
   pl.nseg = static_cast<int>((p->seqlen + pl.seg_len - 1) / pl.seg_len);
   if (pl.nseg > 1) {
-    const size_t bd = static_cast<size_t>(p->batch) * static_cast<size_t>(p->dim);
-    pl.ws_bytes = static_cast<size_t>(pl.nseg) * bd * (static_cast<size_t>(p->dstate) + 1) * sizeof(float);
+    pl.win = static_cast<int>(pl.seg_len < kCorrWindow ? pl.seg_len : kCorrWindow);
+    pl.ws_bytes = seg_layout(pl.nseg, p->batch * p->dim, p->dstate, pl.win).total;
   } else {
     pl.seg_len = p->seqlen;
   }
   return pl;
 }
 
-template <typename TI, typename TY, bool ZOH, bool AGG, bool CONV>
+template <typename TI, typename TY, bool ZOH, int MODE, bool CONV>
 hipError_t launch_scan_t(const ScanArgs& a, dim3 grid, hipStream_t st, bool gate, bool dskip) {
   if (gate && dskip)
-    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, true, true, CONV>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, MODE, true, true, CONV>), grid, dim3(kThreads), 0, st, a);
   else if (gate)
-    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, true, false, CONV>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, MODE, true, false, CONV>), grid, dim3(kThreads), 0, st, a);
   else if (dskip)
-    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, false, true, CONV>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, MODE, false, true, CONV>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, AGG, false, false, CONV>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<TI, TY, ZOH, MODE, false, false, CONV>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename TI, bool ZOH, bool CONV>
-hipError_t launch_scan_io(const ScanArgs& a, dim3 grid, hipStream_t st, bool agg, int ydt, bool gate, bool dskip) {
-  if (agg) return launch_scan_t<TI, float, ZOH, true, CONV>(a, grid, st, false, false);
-  if (ydt == SSM_F32) return launch_scan_t<TI, float, ZOH, false, CONV>(a, grid, st, gate, dskip);
-  return launch_scan_t<TI, uint16_t, ZOH, false, CONV>(a, grid, st, gate, dskip);
+template <typename TI, bool ZOH, bool CONV, int MODE>
+hipError_t launch_scan_io(const ScanArgs& a, dim3 grid, hipStream_t st, int ydt, bool gate, bool dskip) {
+  if (ydt == SSM_F32) return launch_scan_t<TI, float, ZOH, MODE, CONV>(a, grid, st, gate, dskip);
+  return launch_scan_t<TI, uint16_t, ZOH, MODE, CONV>(a, grid, st, gate, dskip);
 }
 
-template <bool CONV>
-hipError_t launch_scan(const ScanArgs& a, dim3 grid, hipStream_t st, bool agg, const ssm_scan_params* p) {
+template <bool CONV, int MODE>
+hipError_t launch_scan(const ScanArgs& a, dim3 grid, hipStream_t st, const ssm_scan_params* p) {
   const bool gate = a.z != nullptr, dskip = a.Dskip != nullptr;
   if (p->io_dtype == SSM_F32) {
-    return p->disc == SSM_DISC_ZOH ? launch_scan_io<float, true, CONV>(a, grid, st, agg, p->y_dtype, gate, dskip)
-                                   : launch_scan_io<float, false, CONV>(a, grid, st, agg, p->y_dtype, gate, dskip);
+    return p->disc == SSM_DISC_ZOH ? launch_scan_io<float, true, CONV, MODE>(a, grid, st, p->y_dtype, gate, dskip)
+                                   : launch_scan_io<float, false, CONV, MODE>(a, grid, st, p->y_dtype, gate, dskip);
   }
-  return p->disc == SSM_DISC_ZOH ? launch_scan_io<uint16_t, true, CONV>(a, grid, st, agg, p->y_dtype, gate, dskip)
-                                 : launch_scan_io<uint16_t, false, CONV>(a, grid, st, agg, p->y_dtype, gate, dskip);
+  return p->disc == SSM_DISC_ZOH ? launch_scan_io<uint16_t, true, CONV, MODE>(a, grid, st, p->y_dtype, gate, dskip)
+                                 : launch_scan_io<uint16_t, false, CONV, MODE>(a, grid, st, p->y_dtype, gate, dskip);
 }
 
 template <typename TI, typename TY, bool ZOH, bool CONV>
@@ -629,25 +760,34 @@ ssm_status run_scan_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, c
     a.conv_silu = conv->activation;
   }
   const size_t bd = static_cast<size_t>(p->batch) * static_cast<size_t>(p->dim);
-  if (pl.nseg > 1) {
-    a.ws_h = static_cast<float*>(workspace);
-    a.ws_sum = a.ws_h + static_cast<size_t>(pl.nseg) * bd * static_cast<size_t>(p->dstate);
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned gx = static_cast<unsigned>((p->dim + kChanPerWG - 1) / kChanPerWG);
   hipError_t e = hipSuccess;
   if (pl.nseg > 1) {
-    e = launch_scan<CONV>(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg - 1)), st, true,
-                          p);
+    // every segment at once (segment 0 from h0, the others from zero), then the chaining of the segments, then the
+    // carry-in's part of each later segment's first `win` steps (and a rescan where it has not decayed by then)
+    const SegLayout l = seg_layout(pl.nseg, static_cast<int64_t>(bd), p->dstate, pl.win);
+    char* w = static_cast<char*>(workspace);
+    a.ws_e = reinterpret_cast<float*>(w + l.e);
+    a.ws_hw = reinterpret_cast<float*>(w + l.hw);
+    a.ws_hin = reinterpret_cast<float*>(w + l.hin);
+    a.ws_sum = reinterpret_cast<float*>(w + l.sum);
+    a.ws_sumw = reinterpret_cast<float*>(w + l.sumw);
+    a.ws_flag = reinterpret_cast<int*>(w + l.flag);
+    a.ws_y0 = reinterpret_cast<float*>(w + l.y0);
+    a.win = pl.win;
+    e = launch_scan<CONV, kSegMain>(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg)), st,
+                                    p);
     if (e == hipSuccess) {
-      const int64_t tot = static_cast<int64_t>(bd) * p->dstate;
-      hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((tot + 255) / 256)), dim3(256), 0, st, A, h0,
-                         a.ws_h, a.ws_sum, p->batch, p->dim, a.N, pl.nseg);
+      hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((bd + 255) / 256)), dim3(256), 0, st, a);
       e = hipGetLastError();
     }
+    if (e == hipSuccess)
+      e = launch_scan<CONV, kSegCorr>(
+          a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg - 1)), st, p);
+  } else {
+    e = launch_scan<CONV, kWhole>(a, dim3(gx, static_cast<unsigned>(p->batch), 1u), st, p);
   }
-  if (e == hipSuccess)
-    e = launch_scan<CONV>(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg)), st, false, p);
   if constexpr (CONV) {
     if (e == hipSuccess && conv->state_out && conv->width > 1) {
       const int64_t rows = static_cast<int64_t>(bd);
