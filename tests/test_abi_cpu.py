@@ -92,19 +92,29 @@ def test_null_params(lib):
     assert lib.ssm_state_update(None, *([None] * 11)) == 1
 
 
+def seg_workspace(nseg, bd, N, win):
+    """Bytes of the segmented scan's workspace: per segment and channel the end state, the zero-start state after the
+    correction window and the carry-in state (N floats each), the two sums of Delta and the rescan flag (one word
+    each), and the window's pre-gate outputs (win floats); every array starts on a 256-byte boundary."""
+    up = lambda v: (v + 255) // 256 * 256
+    return 3 * up(nseg * bd * N * 4) + 3 * up(nseg * bd * 4) + up(nseg * bd * win * 4)
+
+
 def test_workspace_query_and_errors(lib):
     p = P(batch=1, dim=512, seqlen=1 << 20)          # few channels, long sequence: segmented
     nseg = _abi.plan_segments(p)
     assert nseg > 1
     need = _abi.workspace_bytes(p)
-    assert need == nseg * 512 * (16 + 1) * 4
+    seg_len = -(-(1 << 20) // nseg)
+    assert need == seg_workspace(nseg, 512, 16, min(seg_len, 2048))
     assert call_scan(p) == 6                              # no workspace
     assert call_scan(p, ws=FAKE, ws_bytes=need - 1) == 6  # too small
     assert call_scan(p, ws=FAKE + 2, ws_bytes=need) == 5  # misaligned workspace
     q = P(batch=4, dim=5120, seqlen=4096)                 # enough channels: one pass, no workspace
     assert _abi.plan_segments(q) == 1 and _abi.workspace_bytes(q) == 0
     q.segments = 7
-    assert _abi.plan_segments(q) == 7 and _abi.workspace_bytes(q) == 7 * 4 * 5120 * 17 * 4
+    # 64 chunks in 7 segments of 10 chunks (640 steps, all inside the 2048-step correction window)
+    assert _abi.plan_segments(q) == 7 and _abi.workspace_bytes(q) == seg_workspace(7, 4 * 5120, 16, 640)
     q.segments = 10 ** 6                                   # clamped to the number of 64-step chunks
     assert _abi.plan_segments(q) == 4096 // 64
     assert _abi.workspace_bytes(P(dim=0)) == 0 and _abi.plan_segments(P(dim=0)) == 0
