@@ -113,6 +113,20 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt,
                         float* h_final, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssm_scan_fwd for callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace, which is instead a static 64 MiB device array of the
+ * library (one per GPU, held until the process ends).  Nothing is allocated by the call.  When the segmented scan's
+ * workspace would exceed 64 MiB, the correction window of each L-segment shrinks (down to 64 steps) until it fits,
+ * so results may differ from ssm_scan_fwd's within rounding; SSM_ERR_SHAPE when even that does not fit (more than
+ * about 64 MiB / (4 * (64 + 3 * dstate + 3)) segment-channel pairs).  All calls on one GPU share the array: calls that
+ * overlap on the same GPU (different streams, threads or processes) race and must be serialised by the caller.
+ * Other errors as for ssm_scan_fwd; SSM_ERR_HIP if the array's device address cannot be obtained.
+ */
+ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias,
+                                const float* A, const void* B, const void* C, const float* Dskip, const void* z,
+                                const float* h0, void* y, float* h_final, void* stream);
+
+/*
  * Single-token recurrent decode step (constant time and state per token; paper section 1 (ii) and section 2
  * "recurrent mode (2) for autoregressive inference").  Same arithmetic as one step of ssm_scan_fwd.
  *   state [batch][dim][dstate] fp32, read and overwritten in place;  x, dt, z, y [batch][dim];  B, C [batch][dstate];

@@ -19,7 +19,7 @@ EXPORTS = ["ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update", "
            "ssm_abi_version", "ssm_scan_fwd_plan_segments", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_complex_scan_fwd", "ssm_complex_state_update",
            "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan_segments",
-           "ssm_conv1d_fwd", "ssm_conv1d_bwd"]
+           "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_scan_fwd_noalloc"]
 
 
 class Params(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib():
         L.ssm_scan_fwd_plan_segments.restype = ctypes.c_int
         L.ssm_scan_fwd.argtypes = [PP] + [P] * 11 + [P, S, P]
         L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_fwd_noalloc.argtypes = [PP] + [P] * 11 + [P]
+        L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_state_update.argtypes = [PP] + [P] * 11
         L.ssm_state_update.restype = ctypes.c_int
         L.ssm_scan_bwd_workspace_bytes.argtypes = [PP]
@@ -150,6 +152,11 @@ def scan_fwd_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, w
     """Direct call with integer device addresses (0 = NULL)."""
     return lib().ssm_scan_fwd(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
                               workspace_bytes_, stream)
+
+
+def scan_fwd_noalloc_raw(p: Params, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream):
+    """Direct call of the allocation-free forward (the library's static scratch as workspace)."""
+    return lib().ssm_scan_fwd_noalloc(ctypes.byref(p), x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, stream)
 
 
 def make_conv(weight, width, bias=0, state_in=0, state_out=0, activation=1) -> ConvParams:

@@ -616,7 +616,9 @@ inline SegLayout seg_layout(int64_t nseg, int64_t bd, int64_t N, int64_t win) {
   return l;
 }
 
-Plan make_plan(const ssm_scan_params* p) {
+// max_ws: the largest workspace the caller can offer (0 = no limit).  Under a limit the correction window shrinks
+// (to a multiple of the 64-step chunk) until the workspace fits; win = 0 in the result means it cannot fit.
+Plan make_plan(const ssm_scan_params* p, size_t max_ws = 0) {
   Plan pl{1, p->seqlen, 0, 0};
   const int64_t chunks = (p->seqlen + kChunk - 1) / kChunk;
   int64_t nseg = 1;
@@ -640,6 +642,10 @@ Plan make_plan(const ssm_scan_params* p) {
   if (pl.nseg > 1) {
     pl.win = static_cast<int>(pl.seg_len < kCorrWindow ? pl.seg_len : kCorrWindow);
     pl.ws_bytes = seg_layout(pl.nseg, p->batch * p->dim, p->dstate, pl.win).total;
+    while (max_ws > 0 && pl.ws_bytes > max_ws && pl.win > 0) {
+      pl.win -= kChunk;
+      pl.ws_bytes = pl.win > 0 ? seg_layout(pl.nseg, p->batch * p->dim, p->dstate, pl.win).total : 0;
+    }
   } else {
     pl.seg_len = p->seqlen;
   }
@@ -725,11 +731,12 @@ ssm_status check_conv(const ssm_scan_params* p, const ssm_conv_params* c, bool d
 }
 
 // the whole forward call (validation, planning, launches) for the plain (CONV = false) or convolved input
+// scratch_cap > 0: the workspace is the library's static scratch of that many bytes (the plan is fitted to it)
 template <bool CONV>
 ssm_status run_scan_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, const void* x, const void* dt,
                         const float* dt_bias, const float* A, const void* B, const void* C, const float* Dskip,
                         const void* z, const float* h0, void* y, float* h_final, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, size_t scratch_cap = 0) {
   g_err[0] = 0;
   ssm_status s = check_common(p, true);
   if (s != SSM_OK) return s;
@@ -743,7 +750,10 @@ ssm_status run_scan_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, c
       !aligned(y, ys) || !aligned(A, 4) || (dt_bias && !aligned(dt_bias, 4)) || (Dskip && !aligned(Dskip, 4)) ||
       (h0 && !aligned(h0, 4)) || (h_final && !aligned(h_final, 4)))
     return fail(SSM_ERR_ALIGN, "a pointer is not aligned to its element size");
-  const Plan pl = make_plan(p);
+  const Plan pl = make_plan(p, scratch_cap);
+  if (scratch_cap > 0 && pl.nseg > 1 && pl.win <= 0)
+    return fail(SSM_ERR_SHAPE, "%d L-segments of %lld channels need more than the %zu bytes of static scratch", pl.nseg,
+                static_cast<long long>(p->batch * p->dim), scratch_cap);
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes)
       return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes,

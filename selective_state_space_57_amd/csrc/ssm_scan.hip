@@ -24,6 +24,41 @@
 //    carry-in.
 #include "scan_fwd.hpp"
 
+#include <mutex>
+
+namespace {
+
+// Static device scratch of the allocation-free forward (ssm_scan_fwd_noalloc): the segmented scan's workspace for
+// callers that cannot allocate.  Every GPU that runs the library holds one copy until the process ends; calls on the
+// same GPU share it, so calls that overlap on one GPU race.  Nothing in it needs to start at zero (each pass writes
+// what the next one reads), so it is never cleared.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// the device address of `scratch` on each device, looked up once per device with that device current
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+ssm_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return ssm57::fail(SSM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return ssm57::fail(SSM_ERR_HIP, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return ssm57::fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
+}
+
+}  // namespace
+
 namespace ssm57 {
 
 thread_local char g_err[512] = "";
@@ -83,6 +118,19 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt,
                         float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
   return run_scan_fwd<false>(p, nullptr, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, workspace,
                              workspace_bytes, stream);
+}
+
+ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias,
+                                const float* A, const void* B, const void* C, const float* Dskip, const void* z,
+                                const float* h0, void* y, float* h_final, void* stream) {
+  g_err[0] = 0;
+  ssm_status s = check_common(p, true);  // before touching the device: invalid parameters launch nothing
+  if (s != SSM_OK) return s;
+  void* ws = nullptr;
+  s = scratch_for_current_device(&ws);
+  if (s != SSM_OK) return s;
+  return run_scan_fwd<false>(p, nullptr, x, dt, dt_bias, A, B, C, Dskip, z, h0, y, h_final, ws, kScratchBytes, stream,
+                             kScratchBytes);
 }
 
 ssm_status ssm_state_update(const ssm_scan_params* p, float* state, const void* x, const void* dt,

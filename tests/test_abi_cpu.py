@@ -90,6 +90,10 @@ def test_misaligned(lib):
 def test_null_params(lib):
     assert lib.ssm_scan_fwd(None, *([None] * 11), None, 0, None) == 1
     assert lib.ssm_state_update(None, *([None] * 11)) == 1
+    # the allocation-free forward checks its parameters before it touches a device
+    assert lib.ssm_scan_fwd_noalloc(None, *([None] * 11), None) == 1
+    assert lib.ssm_scan_fwd_noalloc(P(seqlen=0), *([None] * 11), None) == 2
+    assert lib.ssm_scan_fwd_noalloc(P(dstate=17), *([None] * 11), None) == 2
 
 
 def seg_workspace(nseg, bd, N, win):
