@@ -40,10 +40,13 @@ struct CScanArgs {
 
 // sin and cos of x by Cody and Waite's reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
 // Functions", 1980): x = k pi/2 + r with pi/2 ~ P1 + P2 (the float nearest pi/2 and the float nearest the remainder,
-// 48 bits together), each step one fused multiply-add; for |x| < 2^22 (|k| < 2.7e6) r is within its rounding plus
-// |k| 1.7e-15 < 5e-9 of the exact reduced argument, under 0.1 ulp of the results; then polynomials on
-// |r| <= pi/4 and the quadrant's swap and signs.  k = rint(x 2/pi) comes from adding 1.5 * 2^23 in the same fused
-// multiply-add: the sum's unit is 1, so it rounds to the nearest integer, and its low mantissa bits hold k mod 4.  The
+// 48 bits together), each step one fused multiply-add, so r is within its own rounding plus |k| 1.7e-15 (an absolute
+// error, at most 5e-9 for |x| < 2^22) of the exact reduced argument; then polynomials on |r| <= pi/4 and the
+// quadrant's swap and signs.  k = rint(x 2/pi) comes from adding 1.5 * 2^23 in the same fused multiply-add: the sum's
+// unit is 1, so it rounds to the nearest integer, and its low mantissa bits hold k mod 4.  The float 2/pi is off by
+// 2^-25 relative, so beyond |x| ~ 10^6 k can miss by one next to a half-integer and |r| reach ~0.96, outside the
+// fitted range.  Measured on the host with these steps emulated in fp32 (tests/test_sincos_cpu.py): within 7e-8
+// absolute of sin and cos for |x| <= 10^6, within 3.1e-7 up to 2^22 (where an fp32 phase has an ulp of 0.25).  The
 // polynomials are minimax fits in r^2 (Lawson's iteratively reweighted least squares, fp64, on [0, pi/4]; the script
 // is sincos_fit.py): sin r / r - 1 to r^6 (relative error 3.6e-9) and cos r - 1 to r^8 (5.4e-11), each a term shorter
 // than Taylor's series for the same accuracy; evaluated in fp32 both stay within 0.9 ulp.  No branch: the general
