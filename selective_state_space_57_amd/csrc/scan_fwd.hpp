@@ -364,59 +364,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   }
 }
 
-// Chains the segments, one thread per channel: h_in[1] = the state at segment 0's end; h_in[s+1] =
-// exp(A * sum_s Delta) h_in[s] + e_s, with e_s segment s's end state from zero (exp(A sum Delta) is the product of
-// the segment's decays); the last one is h_final.  Also decides, per segment s >= 1 with more than `win` steps,
-// whether the carry-in still matters after the window: its part of the state there, |exp(A sum_w Delta) h_in|,
-// summed over n, above 2^-24 of the zero-start state's (so that it could still change a rounded state), or a
-// non-negative A (no decay).
+// Chains the segments, one thread per (channel, state) -- 16 threads per channel, those beyond N idle: h_in[1] = the
+// state at segment 0's end; h_in[s+1] = exp(A * sum_s Delta) h_in[s] + e_s, with e_s segment s's end state from zero
+// (exp(A sum Delta) is the product of the segment's decays); the last one is h_final.  Also decides, per segment
+// s >= 1 with more than `win` steps, whether the carry-in still matters after the window: its part of the state
+// there, |exp(A sum_w Delta) h_in|, summed over n, above 2^-24 of the zero-start state's (so that it could still
+// change a rounded state), or a non-negative A in the channel (no decay).  The loads of segment s + 1 are issued
+// before segment s is chained, so the sequential chain does not wait for memory at every segment.
 __global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
-  const int64_t ch = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t bdN = p.batch * p.dim;
+  const int64_t ch = gid >> 4;  // uniform over each 16-lane group
+  const int n = static_cast<int>(gid & 15);
   if (ch >= bdN) return;
-  const int64_t d = ch % p.dim;
   const int N = p.N;
-  float h[kSub], ap[kSub];
-  bool grows = false;
-#pragma unroll
-  for (int n = 0; n < kSub; ++n) {
-    const float a = n < N ? p.A[d * N + n] : -1.0f;
-    grows = grows || a >= 0.0f;
-    ap[n] = a * kLog2e;
-    h[n] = n < N ? p.ws_e[ch * N + n] : 0.0f;
-  }
+  const bool nv = n < N;
+  const int64_t d = ch % p.dim;
+  const float* __restrict__ E = p.ws_e;
+  const float* __restrict__ HW = p.ws_hw;
+  const float* __restrict__ S = p.ws_sum;
+  const float* __restrict__ SW = p.ws_sumw;
+  float* __restrict__ HIN = p.ws_hin;
+  int* __restrict__ FL = p.ws_flag;
+  const float a = nv ? p.A[d * N + n] : -1.0f;
+  const float ap = a * kLog2e;
+  // any non-negative A among the channel's states (the 16 lanes of the group)
+  float grows = a >= 0.0f ? 1.0f : 0.0f;
+  grows = fmaxf(grows, __shfl_xor(grows, 8, 16));
+  grows = fmaxf(grows, __shfl_xor(grows, 4, 16));
+  grows = fmaxf(grows, __shfl_xor(grows, 2, 16));
+  grows = fmaxf(grows, __shfl_xor(grows, 1, 16));
+  float h = nv ? E[ch * N + n] : 0.0f;
+  auto seg_in = [&](int s, float& e, float& hw, float& sum, float& sumw) {
+    const int64_t o = (static_cast<int64_t>(s) * bdN + ch) * N + n;
+    e = nv ? E[o] : 0.0f;
+    hw = nv ? HW[o] : 0.0f;
+    sum = S[s * bdN + ch];
+    sumw = SW[s * bdN + ch];
+  };
+  float e = 0.0f, hw = 0.0f, sum = 0.0f, sumw = 0.0f;
+  if (p.nseg > 1) seg_in(1, e, hw, sum, sumw);
   for (int s = 1; s < p.nseg; ++s) {
-    const int64_t o = (static_cast<int64_t>(s) * bdN + ch) * N;
+    float e1 = 0.0f, hw1 = 0.0f, sum1 = 0.0f, sumw1 = 0.0f;
+    if (s + 1 < p.nseg) seg_in(s + 1, e1, hw1, sum1, sumw1);  // one segment ahead
     const int64_t ts = static_cast<int64_t>(s) * p.seg_len;
     const int64_t te = ts + p.seg_len < p.L ? ts + p.seg_len : p.L;
-    int flag = 0;
-    if (te - ts > p.win) {
-      const float sw = p.ws_sumw[s * bdN + ch];
-      float cor = 0.0f, ref = 0.0f;
-#pragma unroll
-      for (int n = 0; n < kSub; ++n) {
-        if (n < N) {
-          cor += fabsf(hw_exp2(sw * ap[n]) * h[n]);
-          ref += fabsf(p.ws_hw[o + n]);
-        }
-      }
-      flag = (grows || cor > 0x1p-24f * ref) ? 1 : 0;
-    }
-    p.ws_flag[s * bdN + ch] = flag;
-    const float sum = p.ws_sum[s * bdN + ch];
-#pragma unroll
-    for (int n = 0; n < kSub; ++n) {
-      if (n < N) {
-        p.ws_hin[o + n] = h[n];
-        h[n] = fmaf(hw_exp2(sum * ap[n]), h[n], p.ws_e[o + n]);
-      }
-    }
+    float cor = nv ? fabsf(hw_exp2(sumw * ap) * h) : 0.0f;
+    float ref = fabsf(hw);
+    cor += __shfl_xor(cor, 8, 16); ref += __shfl_xor(ref, 8, 16);
+    cor += __shfl_xor(cor, 4, 16); ref += __shfl_xor(ref, 4, 16);
+    cor += __shfl_xor(cor, 2, 16); ref += __shfl_xor(ref, 2, 16);
+    cor += __shfl_xor(cor, 1, 16); ref += __shfl_xor(ref, 1, 16);
+    if (n == 0) FL[s * bdN + ch] = (te - ts > p.win && (grows > 0.0f || cor > 0x1p-24f * ref)) ? 1 : 0;
+    if (nv) HIN[(static_cast<int64_t>(s) * bdN + ch) * N + n] = h;
+    h = fmaf(hw_exp2(sum * ap), h, e);
+    e = e1; hw = hw1; sum = sum1; sumw = sumw1;
   }
-  if (p.h_final) {
-#pragma unroll
-    for (int n = 0; n < kSub; ++n)
-      if (n < N) p.h_final[ch * N + n] = h[n];
-  }
+  if (p.h_final && nv) p.h_final[ch * N + n] = h;
 }
 
 // ---------------------------------------------------------------------------------------------------------------
@@ -789,7 +793,7 @@ ssm_status run_scan_fwd(const ssm_scan_params* p, const ssm_conv_params* conv, c
     e = launch_scan<CONV, kSegMain>(a, dim3(gx, static_cast<unsigned>(p->batch), static_cast<unsigned>(pl.nseg)), st,
                                     p);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((bd + 255) / 256)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((bd * 16 + 255) / 256)), dim3(256), 0, st, a);
       e = hipGetLastError();
     }
     if (e == hipSuccess)
