@@ -346,7 +346,7 @@ def workload_leg(torch, np, ssm, I, up, w, dev, stream, steps=None, cpu=True, lo
     io = "f32" if w.io == I.F32 else "bf16"
     key = "scan_kernel<%s,%s,euler,gate,dskip> %s" % (io, io, w.name)
     leg = {"workload": w.name, "batch": b, "d_inner": D, "seqlen": L, "d_state": N, "io": io, "segments": nseg,
-           "kernels": ("aggregate pass + carry + scan (one ssm_scan_fwd call)" if nseg > 1 else "scan"),
+           "kernels": ("segments pass + carry + correction pass (one ssm_scan_fwd call)" if nseg > 1 else "scan"),
            "launches": n, "ms_per_step": ms, "warm": pct(per), "elements_per_s": elems / (ms * 1e-3),
            "hbm": hbm_roofline(nbytes, ms, measured_traffic(key), key),
            "roofline": alu_roofline(slots, ms, key, measured_traffic(key))}

@@ -119,7 +119,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_params* p, const void* x, const void* dt,
  * workspace would exceed 64 MiB, the correction window of each L-segment shrinks (down to 64 steps) until it fits,
  * so results may differ from ssm_scan_fwd's within rounding; SSM_ERR_SHAPE when even that does not fit (more than
  * about 64 MiB / (4 * (64 + 3 * dstate + 3)) segment-channel pairs).  All calls on one GPU share the array: calls that
- * overlap on the same GPU (different streams, threads or processes) race and must be serialised by the caller.
+ * overlap on the same GPU (different streams or host threads of one process) race and must be serialised by the caller.
  * Other errors as for ssm_scan_fwd; SSM_ERR_HIP if the array's device address cannot be obtained.
  */
 ssm_status ssm_scan_fwd_noalloc(const ssm_scan_params* p, const void* x, const void* dt, const float* dt_bias,

@@ -161,8 +161,25 @@ __global__ __launch_bounds__(256) void probe_lds_kernel(float* __restrict__ out,
       const uint32_t base = wave * 1024u + ((static_cast<uint32_t>(it) & 3u) * 64u);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if constexpr (KIND == kLdsRead32) {  // (the compiler may pair two reads into one ds_read2st64_b32)
-          acc0 += buf[(base + piece * (step / 4) + static_cast<uint32_t>(u) * 64u) & 4095u];
+        if constexpr (KIND == kLdsRead32) {
+          // written as instructions (a plain loop over repeating addresses is folded by the compiler); the eight
+          // reads are issued back to back and waited for inside the same statement, so no result is in flight
+          // when the statement ends
+          if (u == 0) {
+            const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&buf[base + piece * (step / 4)]));
+            uint32_t r0, r1, r2, r3, r4, r5, r6, r7;
+            asm volatile(
+                "ds_read_b32 %0, %8 offset:0\n\tds_read_b32 %1, %8 offset:256\n\t"
+                "ds_read_b32 %2, %8 offset:512\n\tds_read_b32 %3, %8 offset:768\n\t"
+                "ds_read_b32 %4, %8 offset:1024\n\tds_read_b32 %5, %8 offset:1280\n\t"
+                "ds_read_b32 %6, %8 offset:1536\n\tds_read_b32 %7, %8 offset:1792\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                : "v"(addr)
+                : "memory");
+            acc0 = acc0 + r0 + r1 + r2 + r3;
+            acc1 = acc1 + r4 + r5 + r6 + r7;
+          }
         } else {
           const uint4 v = *reinterpret_cast<const uint4*>(&buf[(base + piece * 4 + static_cast<uint32_t>(u) * 256u) & 4092u]);
           acc0 = acc0 + v.x + v.y;

@@ -154,7 +154,7 @@ def test_layer_workload_full(cfg):
 
 
 def test_million_length_full_and_16_segment_handoff():
-    # one batch element, 512 channels, 2^20 steps: the planner's segmented path (aggregate pass, carry, rescan).
+    # one batch element, 512 channels, 2^20 steps: the planner's segmented path (segments pass, carry, correction).
     # Every output and final state is compared with the oracle, 64 channels at a time (fp64 copies of one block
     # of x, dt, z and y hold 2 GB).
     torch = G.torch_dev()
