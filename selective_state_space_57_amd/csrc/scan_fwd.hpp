@@ -629,10 +629,11 @@ Plan make_plan(const ssm_scan_params* p, size_t max_ws = 0) {
   if (p->segments > 0) {
     nseg = p->segments;
   } else {
-    // fill the 1024 SIMDs: one wave per 4 channels; aim for >= 4096 waves, but keep segments >= 1024 steps
+    // fill the 1024 SIMDs: one wave per 4 channels; aim for 5120 waves (the five per SIMD that the kernel's 96
+    // registers allow), but keep segments >= 1024 steps
     const int64_t waves = ((p->dim + 15) / 16) * p->batch * 4;
     if (waves < 2048) {
-      nseg = (4096 + waves - 1) / waves;
+      nseg = (5120 + waves - 1) / waves;
       const int64_t maxseg = (p->seqlen + 1023) / 1024;
       if (nseg > maxseg) nseg = maxseg;
     }
