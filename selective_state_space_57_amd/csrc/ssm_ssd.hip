@@ -42,19 +42,18 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int kQ = 64;         // chunk length (steps)
 constexpr int kP = 64;         // head width (columns per head)
 constexpr int kThreads = 256;  // 4 waves
-// the 10 lower-triangular 16x16 tiles (row tile tb, column tile sb <= tb) of a 64x64 chunk, index tb (tb + 1) / 2 + sb
-constexpr int kMTiles = 10;
-__host__ __device__ constexpr int mtile_index(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+// the 10 lower-triangular 16x16 tiles of a 64x64 chunk, paired along s: (tb, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr int kMSlots = 6;
+__host__ __device__ constexpr int mslot(int tb, int kk) { return tb + (tb == 3 ? 1 : 0) + kk; }
 
 // LDS.  B, C and x of a chunk are plain copies of their global rows ([s][n] and [s][p]), stored with the 16-byte
 // units of each row permuted (unit u of row r sits at u ^ f(r)) so that both the row-wise operand reads (16 rows, one
-// unit) and the transposing reads (4 rows, several units) hit distinct banks; the global->LDS copy applies the
-// permutation by choosing, per lane, which global unit to fetch.  Each array is single-buffered: every read of a
-// chunk's B, C and x happens before the chunk's second barrier, after which the next chunk's copies are issued, to
-// land during the x M product and the output (and the other workgroups on the CU).  Every buffer is its own
-// __shared__ array, so each access names its buffer statically: the compiler can then tell that a copy in flight
-// into one buffer does not feed a read of another, and does not wait for it.
-struct alignas(16) Scal {   // per-step scalars of a chunk
+// unit) and the transposing reads (4 rows, 2 units) hit distinct banks; the global->LDS copy applies the permutation
+// by choosing, per lane, which global unit to fetch.  B and x are double-buffered, C (whose readers finish before the
+// second barrier of a chunk) is not.  Every buffer is its own __shared__ array and the chunk loop is unrolled by two,
+// so each access names its buffer statically: the compiler can then tell that a copy in flight into one buffer does
+// not feed a read of another, and does not wait for it.
+struct alignas(16) Scal {   // per-step scalars, one private copy per wave
   float ac[kQ];             // A log2(e) cum_s
   float phi[kQ];            // phi_s
   float w[kQ];              // phi_s exp(A (cum_63 - cum_s))
@@ -122,10 +121,8 @@ __device__ __forceinline__ u2 tr16(const uint16_t* p) {
 // Unit permutations (unit u of row r is stored at u ^ f(r)), one per array and its readers, chosen for the LDS of
 // gfx950 (16-byte reads are served 8 lanes at a time over 128 bytes of banks; 8-byte and transposing reads 32 lanes
 // at a time over 256 bytes).  With r = 8a + 4b + 2c + d:
-//   B (16-row reads of one unit, and transposing reads of rows {0..3, 8..11} or {4..7, 12..15} x 4 units, each lane
-//   of a row one half of its unit, even and odd units opposite halves):
-//       f = 8 a + 4 c + 2 b + (d ^ a)      (f & 7 distinct over 8 consecutive rows; over each transposing set f & ~2
-//       distinct, so f ^ g is distinct over the set's rows and g in {0, 2}, or in {1, 3})
+//   B (16-row reads of one unit, and transposing reads of rows {4e..4e+3, 8+4e..} x 2 units):
+//       f = 8 (a ^ b) + 4 c + 2 d + b      (f & 7 distinct over 8 consecutive rows, f >> 1 over the transposing sets)
 //   C (16-row reads only): f = r
 //   x (128-byte rows; transposing reads of rows 4e + {0..3, 8..11} and 4g + {0..3}, and 16-row 8-byte reads):
 //       f = 4 ((r >> 2) ^ (r >> 3)) + 2 c + a
@@ -134,7 +131,7 @@ template <int KIND>
 __device__ __forceinline__ int swz(int r) {
   const int a = (r >> 3) & 1, b = (r >> 2) & 1, c = (r >> 1) & 1, d = r & 1;
   if constexpr (KIND == kSwzB)
-    return 8 * a + 4 * c + 2 * b + (d ^ a);
+    return 8 * (a ^ b) + 4 * c + 2 * d + b;
   else if constexpr (KIND == kSwzC)
     return r & 15;
   else
@@ -223,19 +220,18 @@ __device__ __forceinline__ void lds_barrier() {
 // state and writes the segment's end state and its sum of Delta.  Otherwise the full layer over one segment, starting
 // from h0 carried through the segments before it.
 template <int N, typename TY, bool ZOH, bool GATE, bool DSKIP, bool SEGST>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N <= 128 ? (SEGST ? 4 : 3) : 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N <= 128 ? 2 : 1)))
 ssd_fwd_kernel(SsdArgs a) {
   constexpr int U = N / 8;
   constexpr int NB = N / 16;   // 16-row state tiles per wave
   constexpr int NK = N / 32;   // 32-deep k-steps over the state
-  // One copy of each: every read of a chunk's B, C and x (and of its scalars) happens before the chunk's second
-  // barrier, after which the next chunk's copies are issued (52.75 KB at N = 128: three workgroups per CU).
-  __shared__ alignas(16) uint16_t sB[kQ * N];    // B[s][n]
-  __shared__ alignas(16) uint16_t sX[kQ * kP];   // x[s][p]
-  __shared__ alignas(16) uint16_t sC[kQ * N];    // C[t][n]
-  // M tiles in accumulator layout, per tile [hi, lo] x lane: the 4 bf16 of a lane's part (10 KB)
-  __shared__ u2 sM[kMTiles][2][64];
-  __shared__ Scal sSc;      // per-step scalars of the current chunk
+  __shared__ alignas(16) uint16_t sB0[kQ * N], sB1[kQ * N];    // B[s][n], double-buffered
+  __shared__ alignas(16) uint16_t sX0[kQ * kP], sX1[kQ * kP];  // x[s][p], double-buffered
+  __shared__ alignas(16) uint16_t sC[kQ * N];                  // C[t][n]
+  // M tiles in accumulator layout, paired as operands of the x M product: slot mslot(tb, kk) holds per lane the 4 bf16
+  // of tile (tb, 2 kk) and then those of tile (tb, 2 kk + 1) (zeros where that tile lies above the diagonal), [hi, lo]
+  __shared__ u4 sM[kMSlots][2][64];
+  __shared__ Scal sSc[2];   // per-step scalars of a chunk, computed by wave 0; alternate chunks use alternate copies
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,16 +271,7 @@ ssd_fwd_kernel(SsdArgs a) {
   // transposing reads: lane j of a 16-lane group points at row k0 + j/4, columns 4(j%4) .. +3 of a 16-column tile
   const int trow = l16 >> 2, tcol = 4 * (l16 & 3);
 
-  // State tiles in accumulator layout: hT[nb][c] = S[p = pcol][n = sigma(nb, 4 g4 + c)].  The state update's
-  // output row i of tile nb holds state index sigma(nb, i), a relabelling chosen through the rows of B^T that feed
-  // the product (any bijection works): with i = 4 g + c,
-  //   sigma(nb, 4 g + c) = 8 (4 (nb / 2) + g) + 4 ((g & 1) ^ (nb & 1)) + c,
-  // so that the two tiles 2 kn and 2 kn + 1 together give lane group g the 8 state indices of one 16-byte unit of a
-  // C row (unit 4 kn + g, the halves in the order of g's parity): the C S_prev^T product then reads each operand as
-  // two 8-byte halves of one unit, at offsets that differ per k-step only, and the transposing reads of B^T see each
-  // unit's halves alternate between lanes (no bank conflicts with B's permutation).  h0, h_final and the segment
-  // states are in the natural order of n; nofs(nb) is the first of the four consecutive n of hT[nb] in it.
-  auto nofs = [&](int nb) { return 32 * (nb >> 1) + 8 * g4 + 4 * ((g4 & 1) ^ (nb & 1)); };
+  // state tiles: hT[nb][c] = S[p = pcol][n = 16 nb + 4 g4 + c]
   // (no h0, or the zero-start pass: a zero-length buffer, whose reads return 0)
   const int64_t hcount = int64_t(a.nbh) * kP * N;
   const auto rh0 = make_rsrc(a.h0 && !SEGST ? a.h0 : a.A, a.h0 && !SEGST ? hcount : 0);
@@ -292,15 +279,15 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     hT[nb] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
-                                        rh0, static_cast<int>((srow * N + nofs(nb)) * 4), 0, 0));
+                                        rh0, static_cast<int>((srow * N + 16 * nb + 4 * g4) * 4), 0, 0));
   if constexpr (!SEGST) {
     // carry h0 through the segments before this one: S <- exp(A sum_j Delta) S + (end state of segment j from 0)
     for (int j = 0; j < seg; ++j) {
       const int64_t slot = int64_t(bh) * (a.nseg - 1) + j;
       const float dj = hw_exp2(A2 * a.ws_sum[slot]);
-      const float* st = a.ws_state + (slot * kP + pcol) * N;
+      const float* st = a.ws_state + (slot * kP + pcol) * N + 4 * g4;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) hT[nb] = hT[nb] * dj + *reinterpret_cast<const f4*>(st + nofs(nb));
+      for (int nb = 0; nb < NB; ++nb) hT[nb] = hT[nb] * dj + *reinterpret_cast<const f4*>(st + 16 * nb);
     }
   }
   float dsum = 0.0f;   // sum of Delta over this segment (zero-start pass)
@@ -324,19 +311,15 @@ ssd_fwd_kernel(SsdArgs a) {
   const uint32_t zy_elem = static_cast<uint32_t>(l16) * xrow_e + xcol + static_cast<uint32_t>(16 * wave + 4 * g4);
   const uint32_t z_base = zy_elem * 2u, y_base = zy_elem * static_cast<uint32_t>(sizeof(TY));
   const uint32_t y_row = xrow_e * static_cast<uint32_t>(sizeof(TY));
-  auto stage_chunk = [&](int c) __attribute__((always_inline)) {   // chunk c's B, C and x rows into LDS
-    stage_rows<U>(sB, rB, stB, wave, static_cast<uint32_t>(c * kQ) * bc_row, bc_row);
-    if constexpr (!SEGST) stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(c * kQ) * bc_row, bc_row);
-    stage_rows<8>(sX, rx, stX, wave, static_cast<uint32_t>(c * kQ) * x_row, x_row);
-  };
-  stage_chunk(c0);
+  stage_rows<U>(sB0, rB, stB, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
+  if constexpr (!SEGST) stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(c0 * kQ) * bc_row, bc_row);
+  stage_rows<8>(sX0, rx, stX, wave, static_cast<uint32_t>(c0 * kQ) * x_row, x_row);
   // Per-step scalars of a chunk (Delta, phi, the running sum, decay weights), computed by every wave from dt it loads
-  // itself (one step per lane).  Chunk ck computes those of chunk ck + 1 after its state update, whose matrix products
-  // run meanwhile, so that the dependent chain (softplus, the prefix sum across the wave) is not on the path to a
-  // barrier; wave 0 stores them after the chunk's second barrier (every read of the current ones is done by then) and
-  // the next chunk's first barrier publishes them.
-  struct ScalV { float ac, phi, w; };
-  auto scalars = [&](int c, uint32_t dtv) __attribute__((always_inline)) -> ScalV {
+  // itself, and stored by wave 0.  Chunk ck computes those of chunk ck + 1 after its state update, whose matrix
+  // products run meanwhile, so that the dependent chain (softplus, the prefix sum across the wave) is not on the path
+  // to the chunk barrier; the next chunk's barrier publishes them.  The copy written was last read in the chunk
+  // before, whose readers have all passed the current chunk's barrier.
+  auto scalars = [&](int c, uint32_t dtv, Scal& out) __attribute__((always_inline)) {
     const float u = bf_lo(dtv) + bias;
     float dl = a.softplus ? softplus(u) : u;
     dl = (c * kQ + lane < L) ? dl : 0.0f;
@@ -351,37 +334,45 @@ ssd_fwd_kernel(SsdArgs a) {
     if constexpr (SEGST) {
       if (c < c1) dsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
     }
-    return ScalV{acv, ph, ph * hw_exp2(ac63 - acv)};
-  };
-  auto store_scalars = [&](const ScalV& v) __attribute__((always_inline)) {
+    const float wv = ph * hw_exp2(ac63 - acv);
     if (wave == 0) {
-      sSc.ac[lane] = v.ac;
-      sSc.phi[lane] = v.phi;
-      sSc.w[lane] = v.w;
+      out.ac[lane] = acv;
+      out.phi[lane] = ph;
+      out.w[lane] = wv;
     }
   };
-  store_scalars(scalars(c0, load_dt(c0)));
+  scalars(c0, load_dt(c0), sSc[0]);
+  if constexpr (!SEGST) {
+    if (wave == 0) {   // the halves of the pair slots whose second tile lies above the diagonal stay zero
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        reinterpret_cast<u2*>(&sM[mslot(0, 0)][e][lane])[1] = u2{0u, 0u};
+        reinterpret_cast<u2*>(&sM[mslot(2, 1)][e][lane])[1] = u2{0u, 0u};
+      }
+    }
+  }
 
-  // LDS byte offsets of this lane's C operand halves in the C S_prev^T product: k-step kn reads unit 4 kn + g4 of
-  // row 16 tb + l16, first the half that tile 2 kn holds (g4's parity), then the other.  The permutation of C sees
-  // only the row's low four bits, so the row tile tb is an immediate offset; one register per (kn, half).
-  int coff[SEGST ? 1 : NK][2];
+  // LDS byte offsets of this lane's C operand pieces in the C S_prev^T product, one register each: reads that share a
+  // base register get paired into two-row reads, whose halves then have to be moved into the operand registers
+  int coff[SEGST ? 1 : NK][4][2];
   if constexpr (!SEGST) {
 #pragma unroll
     for (int kn = 0; kn < NK; ++kn)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) coff[kn][j] = opaque(soff<U, kSwzC>(l16, 4 * kn + g4) + 8 * (j ^ (g4 & 1)));
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          coff[kn][tb][j] = opaque(soff<U, kSwzC>(16 * tb + l16, 4 * kn + 2 * j + (g4 >> 1)) + (g4 & 1) * 8);
   }
-  constexpr int kCTile = 16 * U * 16;   // bytes of 16 rows of C
 
-  const uint16_t* const Bc = sB;
-  const uint16_t* const Cc = sC;
-  const uint16_t* const Xc = sX;
-  auto chunk = [&](const int ck) __attribute__((always_inline)) {
+  // one chunk: Bc / Xc hold it, Bn / Xn receive the next one
+  auto chunk = [&](const int ck, const uint16_t* Bc, const uint16_t* Xc, uint16_t* Bn, uint16_t* Xn, Scal& sc,
+                   Scal& scn) __attribute__((always_inline)) {
     const int t0 = ck * kQ;
-    // This wave's copies of chunk ck have landed.  The memory counter completes in issue order, and the last 4
-    // operations of a chunk are the 4 output stores (one per 16-step block, always issued): after the first chunk of
-    // the full pass those may stay in flight.
+    const uint16_t* Cc = sC;
+    // This wave's copies of chunk ck have landed.  The memory counter completes in issue order, and the
+    // last 4 operations of a chunk are the 4 output stores (one per 16-step block, always issued): after the first
+    // chunk of the full pass those may stay in flight.
     if (SEGST || ck == c0)
       wait_vm0();
     else
@@ -392,22 +383,27 @@ ssd_fwd_kernel(SsdArgs a) {
     // global stores, so the barrier leaves the previous chunk's output stores in flight (a workgroup fence would wait
     // for them).
     lds_barrier();
-    // z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3 (issued before the next
-    // chunk's copies: the wait for z then leaves those in flight)
+    // (issued before the next chunk's copies: the wait for z then leaves those in flight)
+    // z at this lane's output positions: t = t0 + 16 tb + l16, p = 16 wave + 4 g4 .. +3
     u2 zo[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      if constexpr (SEGST) {
+        zo[tb] = u2{0u, 0u};
+        continue;
+      }
       const uint32_t o = z_base + static_cast<uint32_t>(t0 + 16 * tb) * x_row;
-      zo[tb] = (GATE && !SEGST)
-                   ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<int>(o), 0, 0))
-                   : u2{0u, 0u};
+      zo[tb] = GATE ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<int>(o), 0, 0))
+                    : u2{0u, 0u};
     }
-    const float* sac = sSc.ac;
+    // the next chunk's copies (past the last chunk they read zeros into a buffer nobody reads)
+    stage_rows<U>(Bn, rB, stB, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
+    stage_rows<8>(Xn, rx, stX, wave, static_cast<uint32_t>(t0 + kQ) * x_row, x_row);
+    const float* sac = sc.ac;
 
-    // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb,
-    // plus D on the diagonal (the skip term D x_t rides in the x M product).  Each wave's tiles are fixed, so every
-    // wave runs its own copy with constant tile coordinates (LDS offsets fold into the instructions; only the four
-    // diagonal tiles mask).  Waves 2 and 3 take three tiles, waves 0 and 1 two.
+    // ---- M tiles: M[t][s] = (C_t . B_s) exp2(ac_t - ac_s) phi_s for s <= t, tile (sb, tb) = index tb(tb+1)/2 + sb.
+    // Each wave's tiles are fixed, so every wave runs its own copy with constant tile coordinates (LDS offsets fold
+    // into the instructions; only the four diagonal tiles mask).  Waves 2 and 3 take three tiles, waves 0 and 1 two.
     auto mtile = [&](auto tic) __attribute__((always_inline)) {
       constexpr int ti = decltype(tic)::value;
       constexpr int tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
@@ -422,20 +418,17 @@ ssd_fwd_kernel(SsdArgs a) {
       // acc[c] = CB[t = 16 tb + l16][s = 16 sb + 4 g4 + c]
       const float act = sac[16 * tb + l16];
       const f4 acs = *reinterpret_cast<const f4*>(&sac[16 * sb + 4 * g4]);
-      const f4 phs = *reinterpret_cast<const f4*>(&sSc.phi[16 * sb + 4 * g4]);
+      const f4 phs = *reinterpret_cast<const f4*>(&sc.phi[16 * sb + 4 * g4]);
       float m[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         m[c] = acc[c] * hw_exp2(act - acs[c]) * phs[c];
-        if constexpr (sb == tb) {
-          m[c] = 4 * g4 + c <= l16 ? m[c] : 0.0f;
-          if constexpr (DSKIP) m[c] += 4 * g4 + c == l16 ? Dh : 0.0f;
-        }
+        if constexpr (sb == tb) m[c] = 4 * g4 + c <= l16 ? m[c] : 0.0f;
       }
       u2 hi, lo;
       split4(m[0], m[1], m[2], m[3], hi, lo);
-      sM[ti][0][lane] = hi;
-      sM[ti][1][lane] = lo;
+      reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][0][lane])[sb & 1] = hi;
+      reinterpret_cast<u2*>(&sM[mslot(tb, sb >> 1)][1][lane])[sb & 1] = lo;
     };
     if constexpr (!SEGST) {
       if (wave == 0) {
@@ -461,15 +454,15 @@ ssd_fwd_kernel(SsdArgs a) {
     for (int tb = 0; tb < 4; ++tb) acc[tb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kn = 0; kn < (SEGST ? 0 : NK); ++kn) {
-      // k-set of this lane: the n of hT[2 kn] (4 values), then those of hT[2 kn + 1]: together unit 4 kn + g4 of C
+      // k-set of this lane: n = 32 kn + 4 g4 + c (tile 2kn) and 32 kn + 16 + 4 g4 + c (tile 2kn+1)
       u2 h0h, h0l, h1h, h1l;
       split4(hT[2 * kn][0], hT[2 * kn][1], hT[2 * kn][2], hT[2 * kn][3], h0h, h0l);
       split4(hT[2 * kn + 1][0], hT[2 * kn + 1][1], hT[2 * kn + 1][2], hT[2 * kn + 1][3], h1h, h1l);
       const u4 hh = cat(h0h, h1h), hl = cat(h0l, h1l);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const u2 c0 = lds8(at(Cc, coff[kn][0] + tb * kCTile));
-        const u2 c1 = lds8(at(Cc, coff[kn][1] + tb * kCTile));
+        const u2 c0 = lds8(at(Cc, coff[kn][tb][0]));
+        const u2 c1 = lds8(at(Cc, coff[kn][tb][1]));
         const u4 bC = cat(c0, c1);
         acc[tb] = mfma(hh, bC, acc[tb]);
         acc[tb] = mfma(hl, bC, acc[tb]);
@@ -480,9 +473,7 @@ ssd_fwd_kernel(SsdArgs a) {
       for (int tb = 0; tb < 4; ++tb) acc[tb] *= hw_exp2(sac[16 * tb + l16]);
     }
 
-    // ---- state update: S_next^T[n][p] = exp2(ac_63) S_prev^T[n][p] + sum_s B^T[n][s] (w_s x[s][p]); output row i of
-    // tile nb is state index sigma(nb, i): lane j of a 16-lane group points at column group g = j % 4 of B's rows,
-    // i.e. half (g & 1) ^ (nb & 1) of unit 4 (nb / 2) + g
+    // ---- state update: S_next^T[n][p] = exp2(ac_63) S_prev^T[n][p] + sum_s B^T[n][s] (w_s x[s][p])
     {
       const float achunk = hw_exp2(sac[kQ - 1]);
       const int xhalf = (tcol & 4) * 2;   // byte offset of columns 4(j%4).. inside their 16-byte unit
@@ -494,7 +485,7 @@ ssd_fwd_kernel(SsdArgs a) {
         for (int e = 0; e < 2; ++e) {
           const int k0 = 32 * ks + 8 * g4 + 4 * e;
           const u2 xv = tr16(at(Xc, soff<8, kSwzX>(k0 + trow, (16 * wave + tcol) >> 3) + xhalf));
-          const f4 wv = *reinterpret_cast<const f4*>(&sSc.w[k0]);
+          const f4 wv = *reinterpret_cast<const f4*>(&sc.w[k0]);
           split4(bf_lo(xv[0]) * wv[0], bf_hi(xv[0]) * wv[1], bf_lo(xv[1]) * wv[2], bf_hi(xv[1]) * wv[3], hp[e],
                  lp[e]);
         }
@@ -504,13 +495,12 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f4 st = hT[nb] * achunk;
-        const int unit = 4 * (nb >> 1) + (l16 & 3);
-        const int bhalf = 8 * ((l16 & 1) ^ (nb & 1));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int k0 = 32 * ks + 8 * g4;
-          const u2 b0 = tr16(at(Bc, soff<U, kSwzB>(k0 + trow, unit) + bhalf));
-          const u2 b1 = tr16(at(Bc, soff<U, kSwzB>(k0 + 4 + trow, unit) + bhalf));
+          const int unit = (16 * nb + tcol) >> 3;
+          const u2 b0 = tr16(at(Bc, soff<U, kSwzB>(k0 + trow, unit) + xhalf));
+          const u2 b1 = tr16(at(Bc, soff<U, kSwzB>(k0 + 4 + trow, unit) + xhalf));
           const u4 aB = cat(b0, b1);
           st = mfma(aB, xh[ks], st);
           st = mfma(aB, xl[ks], st);
@@ -518,52 +508,43 @@ ssd_fwd_kernel(SsdArgs a) {
         hT[nb] = st;
       }
     }
-    const ScalV scn = scalars(ck + 1, dtv);   // the next chunk's, while the state update's products run
-    // x^T operands of the x M product, read now so that x is free after the barrier below:
-    // k-set s = 32 kk + 4 g4 + c (tile 2 kk) and 32 kk + 16 + 4 g4 + c (tile 2 kk + 1)
-    u4 axm[2];
-    if constexpr (!SEGST) {
+    scalars(ck + 1, dtv, scn);              // the next chunk's, while the state update's products run
+    if constexpr (SEGST) return;            // the zero-start pass only carries the state
+    lds_barrier();                          // M tiles are in LDS; every wave is done with C
+    stage_rows<U>(sC, rC, stC, wave, static_cast<uint32_t>(t0 + kQ) * bc_row, bc_row);
+
+    // ---- intra-chunk part: Y^T[p][t] += sum_{s <= t} x^T[p][s] M[t][s]
+    {
       const int xhalf = (tcol & 4) * 2;
-      const int unit = (16 * wave + tcol) >> 3;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        // k-set: s = 32 kk + 4 g4 + c (tile sb = 2kk) and 32 kk + 16 + 4 g4 + c (tile 2kk+1)
+        const int unit = (16 * wave + tcol) >> 3;
         const u2 x0 = tr16(at(Xc, soff<8, kSwzX>(32 * kk + 4 * g4 + trow, unit) + xhalf));
         const u2 x1 = tr16(at(Xc, soff<8, kSwzX>(32 * kk + 16 + 4 * g4 + trow, unit) + xhalf));
-        axm[kk] = cat(x0, x1);
-      }
-    }
-    // Every wave is done with chunk ck's B, C, x and scalars (and has written its M tiles): the next chunk's copies and
-    // scalars may go in.  (No copies after the last chunk: none is left in flight when the workgroup ends.)
-    lds_barrier();
-    store_scalars(scn);
-    if (ck + 1 < c1) stage_chunk(ck + 1);
-    if constexpr (SEGST) return;            // the zero-start pass only carries the state
-
-    // ---- intra-chunk part: Y^T[p][t] += sum_{s <= t} x^T[p][s] M[t][s] (+ D x_t through M's diagonal)
+        const u4 ax = cat(x0, x1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        if (32 * kk > 16 * tb + 15) continue;   // the whole k-step lies above the diagonal
-        // the operand pairs tiles (tb, 2 kk) and (tb, 2 kk + 1); the latter is zero where it lies above the diagonal
-        const bool two = 2 * kk + 1 <= tb;
-        const u2 zero = {0u, 0u};
-        const u4 mh = cat(sM[mtile_index(tb, 2 * kk)][0][lane], two ? sM[mtile_index(tb, 2 * kk + 1)][0][lane] : zero);
-        const u4 ml = cat(sM[mtile_index(tb, 2 * kk)][1][lane], two ? sM[mtile_index(tb, 2 * kk + 1)][1][lane] : zero);
-        acc[tb] = mfma(axm[kk], mh, acc[tb]);
-        acc[tb] = mfma(axm[kk], ml, acc[tb]);
+        for (int tb = 0; tb < 4; ++tb) {
+          if (32 * kk > 16 * tb + 15) continue;   // the whole k-step lies above the diagonal
+          acc[tb] = mfma(ax, sM[mslot(tb, kk)][0][lane], acc[tb]);
+          acc[tb] = mfma(ax, sM[mslot(tb, kk)][1][lane], acc[tb]);
+        }
       }
     }
 
-    // ---- output: acc[tb][c] = Y[t = t0 + 16 tb + l16][p = 16 wave + 4 g4 + c] before the gate
+    // ---- output: acc[tb][c] = Y[t = t0 + 16 tb + l16][p = 16 wave + 4 g4 + c]
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      const int tl = 16 * tb + l16;
+      const u2 xw2 = DSKIP ? lds8(at(Xc, soff<8, kSwzX>(tl, 2 * wave + (g4 >> 1)) + (g4 & 1) * 8)) : u2{0u, 0u};
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t zw = zo[tb][c >> 1];
+        const uint32_t xw = xw2[c >> 1], zw = zo[tb][c >> 1];
+        const float xv = (c & 1) ? bf_hi(xw) : bf_lo(xw);
         const float zv = (c & 1) ? bf_hi(zw) : bf_lo(zw);
         float yv = acc[tb][c];
+        if (DSKIP) yv = fmaf(Dh, xv, yv);
         if (GATE) yv *= silu(zv);
         v[c] = yv;
       }
@@ -576,18 +557,21 @@ ssd_fwd_kernel(SsdArgs a) {
         __builtin_amdgcn_raw_buffer_store_b64(ov, ry, static_cast<int>(o), 0, 0);
       }
     }
-  };
-  for (int ck = c0; ck < c1; ++ck) chunk(ck);
+    };
+  for (int ck = c0; ck < c1; ck += 2) {
+    chunk(ck, sB0, sX0, sB1, sX1, sSc[0], sSc[1]);
+    if (ck + 1 < c1) chunk(ck + 1, sB1, sX1, sB0, sX0, sSc[1], sSc[0]);
+  }
 
   if constexpr (SEGST) {
     const int64_t slot = int64_t(bh) * (a.nseg - 1) + seg;
-    float* st = a.ws_state + (slot * kP + pcol) * N;
+    float* st = a.ws_state + (slot * kP + pcol) * N + 4 * g4;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(st + nofs(nb)) = hT[nb];
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(st + 16 * nb) = hT[nb];
     if (tid == 0) a.ws_sum[slot] = dsum;
   } else if (a.h_final && seg == a.nseg - 1) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(a.h_final + srow * N + nofs(nb)) = hT[nb];
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f4*>(a.h_final + srow * N + 16 * nb + 4 * g4) = hT[nb];
   }
 }
 
