@@ -176,7 +176,8 @@ def issue_rates(torch, dev, stream, iters=4000, reps=3):
         "cycles_per_wave_instruction": {k: res[k]["cycles_per_wave_instruction"]
                                         for k in ("fma", "exp", "mul_dpp_bcast")},
         "memory_bytes_per_clock_per_CU": {k: res[k]["bytes_per_clock_per_CU"]
-                                          for k in ("lds_read_b128", "lds_read_b128_row_broadcast", "lds_write_b32",
+                                          for k in ("lds_read_b128", "lds_read_b128_row_broadcast", "lds_read_b32",
+                                                    "lds_write_b32",
                                                     "lds_write_b64", "lds_write_b128", "vmem_load_b128",
                                                     "vmem_load_b128_row_broadcast")},
         "scan_step_cycles_per_wave": {k: res[k]["cycles_per_wave_step"] for k in ("scan_step_dpp", "scan_step_plain")},
