@@ -249,6 +249,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
       if (MODE == kSegMain) dsum += delta;
+      // the output's gate and skip term, formed now rather than after the gathers below: these instructions then
+      // fill the wait for the block's loads instead of following the contraction (2-4% in an interleaved A/B)
+      const float gz = (GATE && PH != kWindowOut) ? silu(zv) : 1.0f;
+      const float dxs = (DSKIP && PH != kHomog) ? Dv * xv : 0.0f;
 
       // ---- B_n(tb .. tb+15) from LDS
       float bq[kSub];
@@ -321,12 +325,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       if constexpr (PH == kHomog) {
         if (ev) acc += y0row[t - ts];  // the zero-start part (with D x) from the main pass
       } else if (DSKIP) {
-        acc = fmaf(Dv, xv, acc);
+        acc += dxs;
       }
       if constexpr (PH == kWindowOut) {
         if (ev) y0row[t - ts] = acc;  // pre-gate: completed by the correction pass
       } else {
-        if (GATE) acc *= silu(zv);
+        if (GATE) acc *= gz;
         // out-of-range offset for steps outside the segment: the hardware drops the write
         Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
       }
