@@ -261,7 +261,7 @@ def ssd_algorithmic_flops(b, L, H, P, G, N, Q=64):
 
 # the source files each kernel is built from (its translation unit and the headers it includes)
 KERNEL_SOURCES = (("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
-                  ("decode_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
+                  ("decode_", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
                   ("bwd_", ("common.hpp", "ssm_scan_bwd.hip")),
                   ("ssd_", ("common.hpp", "ssm_ssd.hip")),
                   ("complex_", ("common.hpp", "ssm_complex_scan.hip")),
@@ -899,7 +899,7 @@ def main():
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / wd.decode_steps
         dbytes = decode_algorithmic_bytes(wd.batch, wd.dim, wd.dstate)
-        dkey = "decode_kernel<bf16,bf16,euler,vec> decode-b256-d5120"
+        dkey = "decode_vec_kernel<bf16,bf16,euler> decode-b256-d5120"
         out["decode"] = {"workload": "decode-b256-d5120", "steps": wd.decode_steps, "us_per_step": dms * 1e3,
                          "algorithmic_bytes_per_step": dbytes, "achieved_GBps": dbytes / (dms * 1e-3) / 1e9,
                          "frac_of_8TBps": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -57,6 +57,28 @@ def test_decode_equals_scan(io, disc, N):
     assert G.rel_max(G.to_np64(yd), yr) <= G.tol_for(io)
 
 
+@pytest.mark.parametrize("io,disc,gate", [("f32", 0, True), ("bf16", 1, False), ("bf16", 0, False)])
+def test_decode_tile_walk(io, disc, gate):
+    # batch 1001 x 300 channels: 5 channel blocks (the last one 44 channels wide) x 501 batch pairs (the last one
+    # half empty) = 2,505 tiles, several per workgroup of the persistent grid, whose walk wraps the channel-block index
+    torch = G.torch_dev()
+    d = I.random_small(95 + disc, 1001, 300, 1, 16, io=io, h0=True)
+    if not gate:
+        d["z"] = None
+        d["Dskip"] = None
+    dd = G.to_dev(d)
+    state = dd["h0"].clone()
+    sl = lambda k: None if dd[k] is None else dd[k][:, :, 0].contiguous()
+    y = ssm.state_update(state, sl("x"), sl("dt"), dd["A"], sl("B"), sl("C"), dt_bias=dd["dt_bias"],
+                         Dskip=dd["Dskip"], z=sl("z"), y_dtype=torch.float32, disc=disc)
+    f = I.as_f64(d)
+    fz = None if f["z"] is None else f["z"][:, :, 0]
+    yr, sr = oracle.state_update(f["h0"], f["x"][:, :, 0], f["dt"][:, :, 0], f["A"], f["B"][:, :, 0],
+                                 f["C"][:, :, 0], dt_bias=f["dt_bias"], Dskip=f["Dskip"], z=fz, disc=disc)
+    assert G.rel_max(G.to_np64(y), yr) <= G.tol_for(io)
+    assert G.rel_max(G.to_np64(state), sr) <= G.tol_for(io)
+
+
 def test_decode_bf16_output():
     torch = G.torch_dev()
     d = I.random_small(70, 2, 77, 1, 16, io="bf16", h0=True)
