@@ -57,12 +57,15 @@ def test_decode_equals_scan(io, disc, N):
     assert G.rel_max(G.to_np64(yd), yr) <= G.tol_for(io)
 
 
-@pytest.mark.parametrize("io,disc,gate", [("f32", 0, True), ("bf16", 1, False), ("bf16", 0, False)])
-def test_decode_tile_walk(io, disc, gate):
+@pytest.mark.parametrize("batch,dim,io,disc,gate", [(1001, 300, "f32", 0, True), (1001, 300, "bf16", 1, False),
+                                                    (1001, 300, "bf16", 0, False), (3, 70000, "bf16", 0, True)])
+def test_decode_tile_walk(batch, dim, io, disc, gate):
     # batch 1001 x 300 channels: 5 channel blocks (the last one 44 channels wide) x 501 batch pairs (the last one
-    # half empty) = 2,505 tiles, several per workgroup of the persistent grid, whose walk wraps the channel-block index
+    # half empty) = 2,505 tiles, several per workgroup of the persistent grid, whose walk wraps the channel-block
+    # index.  3 x 70,000: 1,094 channel blocks (more than the grid's workgroups) x 2 batch pairs, so a workgroup's
+    # step advances the channel block alone and wraps into the next batch pair.
     torch = G.torch_dev()
-    d = I.random_small(95 + disc, 1001, 300, 1, 16, io=io, h0=True)
+    d = I.random_small(95 + disc + dim % 7, batch, dim, 1, 16, io=io, h0=True)
     if not gate:
         d["z"] = None
         d["Dskip"] = None
