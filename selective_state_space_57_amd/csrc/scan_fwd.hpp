@@ -80,9 +80,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   const int tid = threadIdx.x;
   const int n = tid & 15;    // state index of this lane; also the step index it owns within a 16-step block
   const int row = tid >> 4;  // channel within the workgroup
-  const int64_t d = static_cast<int64_t>(blockIdx.x) * kChanPerWG + row;
-  const int64_t b = blockIdx.y;
-  const int seg = MODE == kSegCorr ? static_cast<int>(blockIdx.z) + 1 : static_cast<int>(blockIdx.z);
+  // Workgroup order: the grid is (channel group, batch, segment), but workgroups with consecutive linear ids go to
+  // the eight XCDs in turn, each with its own L2.  So the linear id i is mapped to the tile j that gives every XCD a
+  // contiguous run of tiles (XCD i mod 8 takes the (i mod 8)-th run, in order): the workgroups that stage the same B
+  // and C rows (one batch element and segment) then share one L2 instead of fetching those rows into all eight.
+  int64_t wx, b;  // channel group, batch element
+  int wz;         // segment
+  {
+    const uint64_t gx = gridDim.x, gy = gridDim.y;
+    const uint64_t G = gx * gy * gridDim.z;
+    const uint64_t wi = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const uint64_t q8 = G >> 3, r8 = G & 7, xcd = wi & 7, k8 = wi >> 3;
+    const uint64_t wj = xcd < r8 ? xcd * (q8 + 1) + k8 : r8 * (q8 + 1) + (xcd - r8) * q8 + k8;
+    if (G <= 0xffffffffull) {  // uniform; 32-bit divisions
+      const uint32_t j32 = static_cast<uint32_t>(wj), gx32 = gridDim.x, gy32 = gridDim.y;
+      const uint32_t yz = j32 / gx32;
+      wx = j32 - yz * gx32;
+      b = yz % gy32;
+      wz = static_cast<int>(yz / gy32);
+    } else {
+      const uint64_t yz = wj / gx;
+      wx = static_cast<int64_t>(wj - yz * gx);
+      b = static_cast<int64_t>(yz % gy);
+      wz = static_cast<int>(yz / gy);
+    }
+  }
+  const int64_t d = wx * kChanPerWG + row;
+  const int seg = MODE == kSegCorr ? wz + 1 : wz;
   const bool chv = d < p.dim;
   const bool nv = n < p.N;
   const int64_t ch = b * p.dim + d;
@@ -94,7 +118,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   const int tw = (MODE != kWhole && seg > 0) ? (ts + p.win < te ? ts + p.win : te) : ts;
 
   // descriptors start at the workgroup's first channel row (x, dt, z, y) and at the batch's B / C rows
-  const int64_t row0 = b * p.dim + static_cast<int64_t>(blockIdx.x) * kChanPerWG;
+  const int64_t row0 = b * p.dim + wx * kChanPerWG;
   const int64_t rows_left = p.batch * p.dim - row0;
   const auto rx_ = make_rsrc(static_cast<const TI*>(p.x) + row0 * p.L, rows_left * p.L);
   const auto rd_ = make_rsrc(static_cast<const TI*>(p.dt) + row0 * p.L, rows_left * p.L);
@@ -191,7 +215,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     return v;
   };
 
-  const bool wg_full = static_cast<int64_t>(blockIdx.x) * kChanPerWG + kChanPerWG <= p.dim && p.N == kSub;
+  const bool wg_full = wx * kChanPerWG + kChanPerWG <= p.dim && p.N == kSub;
 
   // one 64-step chunk; FULL: every step and every channel / state of the workgroup is valid, so no masking.
   // PH = kFullInput: the scan as defined; kWindowOut: the same, but the pre-gate output goes to ws_y0; kHomog: no
@@ -213,6 +237,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     const bool more = t0 + kChunk < tend;  // uniform
     if (more) fetch_staged(t0 + kChunk);
 
+    float ypend = 0.0f;  // full chunks: an even block's output, stored with the next block's
+    static_assert((kChunk / kSub) % 2 == 0, "blocks are stored in pairs");
 #pragma unroll
     for (int s = 0; s < kChunk / kSub; ++s) {
       const int tb = t0 + s * kSub;
@@ -331,8 +357,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
         if (ev) y0row[t - ts] = acc;  // pre-gate: completed by the correction pass
       } else {
         if (GATE) acc *= gz;
-        // out-of-range offset for steps outside the segment: the hardware drops the write
-        Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
+        if constexpr (FULL) {
+          // the outputs of blocks 2i and 2i + 1 are stored together: the row's two 32-byte pieces then reach the L2
+          // together and leave it as one 64-byte write, rather than as separate partial writes of one line
+          if (s % 2 == 0) {
+            ypend = acc;
+          } else {
+            Buf<TY>::st(ry_, lane_yo + static_cast<uint32_t>(tb - kSub) * SY, ypend);
+            Buf<TY>::st(ry_, lane_yo + static_cast<uint32_t>(tb) * SY, acc);
+          }
+        } else {
+          // out-of-range offset for steps outside the segment: the hardware drops the write
+          Buf<TY>::st(ry_, ev ? lane_yo + static_cast<uint32_t>(tb) * SY : kDropOffset, acc);
+        }
       }
     }
   };
