@@ -107,7 +107,8 @@ PROBE_KINDS = (("fma", 0), ("exp", 1), ("mix_exp_fma_1_1", 2), ("mix_exp_fma_1_3
                ("split_waves_exp_fma", 6), ("mul_dpp_bcast", 7), ("lds_read_b128", 8),
                ("lds_read_b128_row_broadcast", 9), ("lds_write_b32", 10), ("lds_read_b32", 11),
                ("scan_step_dpp", 12), ("scan_step_plain", 13), ("vmem_load_b128", 14),
-               ("vmem_load_b128_row_broadcast", 15), ("lds_write_b64", 16), ("lds_write_b128", 17))
+               ("vmem_load_b128_row_broadcast", 15), ("lds_write_b64", 16), ("lds_write_b128", 17),
+               ("scan_step_wave_combine", 18))
 # bytes one wave moves per LDS (or vector-memory) instruction of each memory probe kind
 PROBE_LDS_BYTES = {8: 64 * 16, 9: 64 * 16, 10: 64 * 4, 11: 64 * 4, 14: 64 * 16, 15: 64 * 16, 16: 64 * 8,
                    17: 64 * 16}
@@ -150,7 +151,7 @@ def issue_rates(torch, dev, stream, iters=4000, reps=3):
             r = {"ms": ms, "shader_clock_GHz": ghz, "instructions_per_wave": ops[0] * iters,
                  "bytes_per_clock_per_CU": ops[0] * iters * waves * PROBE_LDS_BYTES[kind] / 256 / cycles_per_simd,
                  "cycles_per_wave_instruction_per_CU": cycles_per_simd * 256 / (ops[0] * iters * waves)}
-        elif kind in (12, 13):        # SIMD cycles per wave and state step
+        elif kind in (12, 13, 18):    # SIMD cycles per wave and state step (64 lanes x one state step each)
             r = {"ms": ms, "shader_clock_GHz": ghz,
                  "cycles_per_wave_step": cycles_per_simd * 1024 / (waves * iters * ops[1])}
         else:
@@ -180,7 +181,8 @@ def issue_rates(torch, dev, stream, iters=4000, reps=3):
                                                     "lds_write_b32",
                                                     "lds_write_b64", "lds_write_b128", "vmem_load_b128",
                                                     "vmem_load_b128_row_broadcast")},
-        "scan_step_cycles_per_wave": {k: res[k]["cycles_per_wave_step"] for k in ("scan_step_dpp", "scan_step_plain")},
+        "scan_step_cycles_per_wave": {k: res[k]["cycles_per_wave_step"]
+                                      for k in ("scan_step_dpp", "scan_step_plain", "scan_step_wave_combine")},
         "shader_clock_GHz_under_fma_load": res["fma"]["shader_clock_GHz"],
         "wall_clock_kHz": wall_khz, "iters": iters, "lanes": lanes,
         "kernels": res,

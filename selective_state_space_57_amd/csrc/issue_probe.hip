@@ -40,6 +40,11 @@ enum Kind : int {
   kVmemLoad128Bc = 15,  // the same, each 16-lane row of a wave loading the same 16 pieces (256 distinct bytes)
   kLdsWrite64 = 16,     // ds_write_b64, 64 consecutive pieces per wave
   kLdsWrite128 = 17,    // ds_write_b128, 64 consecutive pieces per wave
+  kCoreCombine = 18,    // the same recurrence parallel in time: a wave's 64 lanes hold 64 consecutive steps of one
+                        // state; per lane a = exp2(D A'), b = (D X) B, then an inclusive scan of the (a, b) pairs over
+                        // the 64 lanes with (a1, b1) o (a2, b2) = (a2 a1, a2 b1 + b2) (DPP row_shr 1, 2, 4, 8, then
+                        // row_bcast 15 and 31), h = a h_in + b with h_in the previous chunk's last state (readlane),
+                        // y = fma(C, h, y); four independent states per wave, so four such chunks per iteration
 };
 
 template <int K>
@@ -136,6 +141,19 @@ __global__ __launch_bounds__(256) void probe_kernel(float* __restrict__ out, uns
     clk[2 * blockIdx.x] = __builtin_amdgcn_s_memtime() - c0;
     clk[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime() - r0;
   }
+}
+
+// one level of the inclusive scan: combine with the pair of the lane CTRL selects (DPP control word, under the row
+// mask RM); lanes without a source take the identity (1, 0)
+template <int CTRL, int RM>
+__device__ __forceinline__ void combine_level(float& a, float& b) {
+  const float pa = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f),
+                                                                        __builtin_bit_cast(int, a), CTRL, RM, 0xf,
+                                                                        false));
+  const float pb = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, b), CTRL, RM, 0xf,
+                                                                        false));
+  b = fmaf(a, pb, b);
+  a = a * pa;
 }
 
 // LDS throughput and the scan's inner step.  Each workgroup owns 16 KB of LDS; a loop iteration issues 8 LDS
@@ -286,6 +304,38 @@ __global__ __launch_bounds__(256) void probe_lds_kernel(float* __restrict__ out,
       }
     }
     res = h + y;
+  } else if constexpr (KIND == kCoreCombine) {
+    const int lane = tid & 63;
+    float ap[4], bt[4], ct[4], hc[4], y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ap[j] = -1.4f - 1e-3f * static_cast<float>(lane) - 0.1f * static_cast<float>(j);
+      bt[j] = 0.5f + 1e-3f * static_cast<float>(lane) + 0.01f * static_cast<float>(j) + seed;
+      ct[j] = 0.25f - 1e-3f * static_cast<float>(lane) - 0.01f * static_cast<float>(j) + seed;
+      hc[j] = 0.0f;
+      y[j] = 0.0f;
+    }
+    float d = 0.01f + 1e-5f * static_cast<float>(lane) + seed, x = 0.1f + seed;
+    for (int it = 0; it < iters; ++it) {
+      // this chunk's per-step inputs: opaque to the compiler, so nothing is hoisted out of the loop
+      asm volatile("" : "+v"(d), "+v"(x));
+      const float dx = d * x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a = __builtin_amdgcn_exp2f(d * ap[j]);
+        float b = dx * bt[j];
+        combine_level<0x111, 0xf>(a, b);  // row_shr:1
+        combine_level<0x112, 0xf>(a, b);  // row_shr:2
+        combine_level<0x114, 0xf>(a, b);  // row_shr:4
+        combine_level<0x118, 0xf>(a, b);  // row_shr:8
+        combine_level<0x142, 0xa>(a, b);  // row_bcast:15 into rows 1 and 3
+        combine_level<0x143, 0xc>(a, b);  // row_bcast:31 into rows 2 and 3
+        const float h = fmaf(a, hc[j], b);
+        y[j] = fmaf(ct[j], h, y[j]);
+        hc[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h), 63));
+      }
+    }
+    res = (y[0] + y[1]) + (y[2] + y[3]) + hc[0];
   }
   __syncthreads();
   out[blockIdx.x * 256 + tid] = static_cast<float>(acc0 ^ acc1) + res;
@@ -321,6 +371,7 @@ void ssm_probe_ops_per_iter(int kind, int ops[3]) {
       ops[0] = 8;  // LDS or vector-memory instructions
       break;
     case kCoreDpp: case kCorePlain: ops[1] = 16; break;  // state steps (one exp each) per iteration
+    case kCoreCombine: ops[1] = 4; break;                  // state steps per lane per iteration (4 chunks)
     default: break;
   }
 }
@@ -357,6 +408,9 @@ int ssm_probe_launch(int kind, int iters, float* out, unsigned long long* clk, v
     case kLdsRead32: hipLaunchKernelGGL(probe_lds_kernel<kLdsRead32>, grid, block, 0, st, out, clk, iters, 0.0f); break;
     case kCoreDpp: hipLaunchKernelGGL(probe_lds_kernel<kCoreDpp>, grid, block, 0, st, out, clk, iters, 0.0f); break;
     case kCorePlain: hipLaunchKernelGGL(probe_lds_kernel<kCorePlain>, grid, block, 0, st, out, clk, iters, 0.0f); break;
+    case kCoreCombine:
+      hipLaunchKernelGGL(probe_lds_kernel<kCoreCombine>, grid, block, 0, st, out, clk, iters, 0.0f);
+      break;
     case kVmemLoad128:
       hipLaunchKernelGGL(probe_lds_kernel<kVmemLoad128>, grid, block, 0, st, out, clk, iters, 0.0f);
       break;
