@@ -38,12 +38,11 @@ using namespace ssm57;
 constexpr int kBT = 64;              // steps per chunk
 constexpr int kBlk = 16;             // steps per block (= lanes per row)
 constexpr int kNB = kBT / kBlk;      // blocks per chunk
-// Per (channel, chunk) record of side values, 6 slots of 16 floats (384 bytes, a multiple of the 128-byte line): slot 0
-// the chunk's end state from a zero start (the carry turns it into the entering state), slot 1 lambda (turned into
-// the entering adjoint), slots 2..4 the local states after blocks 0..kNB-2, slot 5 padding.  The carry touches only
-// slots 0 and 1, which share one line.
-constexpr int kRec = 6;
-constexpr int kSlotIn = 0, kSlotLam = 1, kSlotLoc = 2;
+// Side values per (channel, chunk), 16 floats each: in sideE the chunk's end state from a zero start (the carry turns
+// it into the entering state), in sideL lambda (turned into the entering adjoint), each array chunk-major per channel
+// so that the carry's chains read whole 128-byte lines (two chunks each); in `side` a record of 4 slots (256 bytes,
+// two lines): the local states after blocks 0..kNB-2, then padding.
+constexpr int kRec = 4;
 constexpr int kNP = 16;              // state axis padded to 16 in workspace arrays
 constexpr int kSStride = kBT + 4;    // sB / sC row stride (floats): conflict-free b128 reads along t
 constexpr int kTStride = kNP + 4;    // sBt / sCt ([t][n] copies) step stride: conflict-free b128 reads along n
@@ -73,7 +72,9 @@ struct BwdArgs {
   float* dD;
   float* dbias;
   float* dh0;
-  float* side;    // [batch*dim][nck][kRec][16]
+  float* side;    // [batch*dim][nck][kRec][16]: local block-start states
+  float* sideE;   // [batch*dim][nck][16]: end state from zero, then the state entering the chunk
+  float* sideL;   // [batch*dim][nck][16]: lambda, then the adjoint entering the chunk from later chunks
   float* cum;     // [batch*dim][nck][kNB]: sum of Delta from the chunk start through block i
   float* partBC;  // [G][batch][2][16][Lpad]: per-workgroup dB (0) / dC (1)
   float* partA;   // [batch*nck][dim][16]
@@ -83,6 +84,31 @@ struct BwdArgs {
 };
 
 __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// Workgroup order of prep and main, whose grid is (chunk, channel group, batch).  Workgroups with consecutive linear
+// ids go to the eight XCDs in turn, each with its own L2; the linear id i is mapped to the tile that gives XCD i mod 8
+// a contiguous run of tiles, chunk fastest.  The chunks of one channel group then share an L2: their records of
+// Delta sums (16 bytes per chunk) share 128-byte lines, which the grid's own order (XCD = chunk mod 8) fetched into
+// every XCD.
+__device__ __forceinline__ void bwd_tile(int& k, int& g, int64_t& b) {
+  const uint64_t gx = gridDim.x, gy = gridDim.y;
+  const uint64_t G = gx * gy * gridDim.z;
+  const uint64_t wi = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint64_t q8 = G >> 3, r8 = G & 7, xcd = wi & 7, k8 = wi >> 3;
+  const uint64_t wj = xcd < r8 ? xcd * (q8 + 1) + k8 : r8 * (q8 + 1) + (xcd - r8) * q8 + k8;
+  if (G <= 0xffffffffull) {  // uniform; 32-bit divisions
+    const uint32_t j32 = static_cast<uint32_t>(wj), gx32 = gridDim.x, gy32 = gridDim.y;
+    const uint32_t yz = j32 / gx32;
+    k = static_cast<int>(j32 - yz * gx32);
+    g = static_cast<int>(yz % gy32);
+    b = yz / gy32;
+  } else {
+    const uint64_t yz = wj / gx;
+    k = static_cast<int>(wj - yz * gx);
+    g = static_cast<int>(yz % gy);
+    b = static_cast<int64_t>(yz / gy);
+  }
+}
 
 // B and C of one chunk into LDS as fp32, [n][t]; zero outside the sequence and the state range
 template <typename TI>
@@ -227,8 +253,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so per-quad descriptors are SGPRs
   const int n = lane & 15, r = lane >> 4;
-  const int k = blockIdx.x, g = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  int k, g;
+  int64_t b;
+  bwd_tile(k, g, b);
   const int L = static_cast<int>(p.L);
   const int t0 = k * kBT;
   const bool nv = n < p.N;
@@ -248,8 +275,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     const float Ap = An * kLog2e;
     const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
     const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
-    float* const sp = p.side + (bd * p.nck + k) * (kRec * kNP) + n;
-    float* const cp = p.cum + (bd * p.nck + k) * kNB;
+    const int64_t rec = bd * p.nck + k;
+    float* const sp = p.side + rec * (kRec * kNP) + n;
+    float* const cp = p.cum + rec * kNB;
     const int boff = opaque(n * kSStride);
     float h = 0.0f, E = 1.0f, lam = 0.0f, cum = 0.0f;
     static_for<kNB>([&](auto ic) {
@@ -303,7 +331,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
       s += __shfl_xor(s, 1, 16);
       cum += s;
       if (chv) {
-        sp[(I == kNB - 1 ? kSlotIn : kSlotLoc + I) * kNP] = h;
+        if constexpr (I == kNB - 1)
+          p.sideE[rec * kNP + n] = h;
+        else
+          sp[I * kNP] = h;
         if (n == 0) cp[I] = cum;
       }
       pin(h);
@@ -311,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
       pin(lam);
       pin(cum);
     });
-    if (chv) sp[kSlotLam * kNP] = lam;
+    if (chv) p.sideL[rec * kNP + n] = lam;
   }
 }
 
@@ -327,21 +358,23 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
   if (bd >= p.batch * p.dim || n >= p.N) return;
   const int64_t d = bd % p.dim;
   const float Ap = p.A[d * p.N + n] * kLog2e;
-  float* const sp = p.side + bd * p.nck * (kRec * kNP) + n;
+  float* const ep = p.sideE + bd * p.nck * kNP + n;
+  float* const lp = p.sideL + bd * p.nck * kNP + n;
   const float* const cp = p.cum + bd * p.nck * kNB + (kNB - 1);
-  auto slot = [&](int k, int j) { return sp + static_cast<int64_t>(k) * (kRec * kNP) + j * kNP; };
+  auto slotE = [&](int k) { return ep + static_cast<int64_t>(k) * kNP; };
+  auto slotL = [&](int k) { return lp + static_cast<int64_t>(k) * kNP; };
   float hs = p.h0 ? p.h0[bd * p.N + n] : 0.0f;
   for (int k0 = 0; k0 < p.nck; k0 += U) {
     float e[U], P[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = k0 + u < p.nck;
-      e[u] = ok ? *slot(k0 + u, kSlotIn) : 0.0f;
+      e[u] = ok ? *slotE(k0 + u) : 0.0f;
       P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k0 + u) * kNB] * Ap) : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k0 + u < p.nck) *slot(k0 + u, kSlotIn) = hs;
+      if (k0 + u < p.nck) *slotE(k0 + u) = hs;
       hs = fmaf(P[u], hs, e[u]);
     }
   }
@@ -351,12 +384,12 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = k1 - u >= 0;
-      l[u] = ok ? *slot(k1 - u, kSlotLam) : 0.0f;
+      l[u] = ok ? *slotL(k1 - u) : 0.0f;
       P[u] = ok ? hw_exp2(cp[static_cast<int64_t>(k1 - u) * kNB] * Ap) : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k1 - u >= 0) *slot(k1 - u, kSlotLam) = rho;
+      if (k1 - u >= 0) *slotL(k1 - u) = rho;
       rho = fmaf(P[u], rho, l[u]);
     }
   }
@@ -376,8 +409,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so per-quad descriptors are SGPRs
   const int n = lane & 15, r = lane >> 4;
-  const int k = blockIdx.x, g = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  int k, g;
+  int64_t b;
+  bwd_tile(k, g, b);
   const int L = static_cast<int>(p.L);
   const int t0 = k * kBT;
   const bool nv = n < p.N;
@@ -409,14 +443,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int64_t d = chan(q);
     const bool ok = q < p.Q && d < p.dim;
     const int64_t bd = b * p.dim + (ok ? d : 0);
-    const float* sp = p.side + (bd * p.nck + k) * (kRec * kNP) + n;
-    const float* cp = p.cum + (bd * p.nck + k) * kNB;
-    s.hin = (ok && nv) ? sp[kSlotIn * kNP] : 0.0f;
-    s.rho = (ok && nv) ? sp[kSlotLam * kNP] : 0.0f;
+    const int64_t rec = bd * p.nck + k;
+    const float* sp = p.side + rec * (kRec * kNP) + n;
+    const float* cp = p.cum + rec * kNB;
+    s.hin = (ok && nv) ? p.sideE[rec * kNP + n] : 0.0f;
+    s.rho = (ok && nv) ? p.sideL[rec * kNP + n] : 0.0f;
     s.hl[0] = s.cm[0] = 0.0f;
 #pragma unroll
     for (int i = 1; i < kNB; ++i) {
-      s.hl[i] = (ok && nv) ? sp[(kSlotLoc + i - 1) * kNP] : 0.0f;
+      s.hl[i] = (ok && nv) ? sp[(i - 1) * kNP] : 0.0f;
       s.cm[i] = ok ? cp[i - 1] : 0.0f;
     }
     return s;
@@ -694,7 +729,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs p) {
 struct BwdPlan {
   int nck, Q, G;
   int64_t Lpad;
-  size_t off_side, off_cum, off_bc, off_a, off_p, bytes;
+  size_t off_side, off_e, off_l, off_cum, off_bc, off_a, off_p, bytes;
 };
 
 BwdPlan make_bwd_plan(const ssm_scan_params* p) {
@@ -715,6 +750,10 @@ BwdPlan make_bwd_plan(const ssm_scan_params* p) {
   size_t off = 0;
   pl.off_side = off;
   off += up(bd * nck * kRec * kNP);
+  pl.off_e = off;
+  off += up(bd * nck * kNP);
+  pl.off_l = off;
+  off += up(bd * nck * kNP);
   pl.off_cum = off;
   off += up(bd * nck * kNB);
   pl.off_bc = off;
@@ -788,7 +827,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_params* p, const void* x, const void* dt,
   a.dt_bias = dt_bias; a.A = A; a.Dskip = Dskip; a.h0 = h0; a.dh_final = dh_final;
   a.dx = dx; a.ddt = ddt; a.dz = dz; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dDskip; a.dbias = ddt_bias; a.dh0 = dh0;
   float* ws = static_cast<float*>(workspace);
-  a.side = ws + pl.off_side; a.cum = ws + pl.off_cum; a.partBC = ws + pl.off_bc; a.partA = ws + pl.off_a;
+  a.side = ws + pl.off_side; a.sideE = ws + pl.off_e; a.sideL = ws + pl.off_l; a.cum = ws + pl.off_cum; a.partBC = ws + pl.off_bc; a.partA = ws + pl.off_a;
   a.partP = ws + pl.off_p;
   a.batch = p->batch; a.dim = p->dim; a.L = p->seqlen; a.Lpad = pl.Lpad;
   a.N = static_cast<int>(p->dstate); a.nck = pl.nck; a.Q = pl.Q; a.G = pl.G; a.softplus = p->dt_softplus;
