@@ -112,8 +112,19 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
   __shared__ __align__(16) float sY[kCBlk * kCRow];      // per row: Re(C_n h_n) as [t][n]
   const int tid = threadIdx.x;
   const int n = tid & 15, row = tid >> 4;
-  const int64_t d = static_cast<int64_t>(blockIdx.x) * 16 + row;
-  const int64_t b = blockIdx.y;
+  // Workgroup order: workgroups with consecutive linear ids go to the eight XCDs in turn, each with its own L2; the
+  // linear id i is mapped to the tile that gives XCD i mod 8 a contiguous run of (channel group, batch) tiles, so the
+  // workgroups that stage one batch element's B and C share an L2 instead of fetching those rows into all eight.
+  int64_t wx, b;
+  {
+    const uint32_t gx = gridDim.x, G = gridDim.x * gridDim.y;  // the host keeps G below 2^32
+    const uint32_t wi = blockIdx.x + gx * blockIdx.y;
+    const uint32_t q8 = G >> 3, r8 = G & 7, xcd = wi & 7, k8 = wi >> 3;
+    const uint32_t wj = xcd < r8 ? xcd * (q8 + 1) + k8 : r8 * (q8 + 1) + (xcd - r8) * q8 + k8;
+    b = wj / gx;
+    wx = wj - static_cast<uint32_t>(b) * gx;
+  }
+  const int64_t d = wx * 16 + row;
   const bool chv = d < p.dim, nv = n < p.N;
   const int64_t ch = b * p.dim + d;
   const int L = static_cast<int>(p.L);
@@ -155,6 +166,11 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
   float2 nb, nc;
   float nx, nd, nz;
   fetch(0, nb, nc, nx, nd, nz);
+  // the output of every other block waits for the next block's, so that the two 32-byte pieces of each row leave the
+  // L2 together as one 64-byte write rather than as separate partial writes of one line
+  float ypend = 0.0f;
+  bool yok = false, pend = false;
+  int tpend = 0;
 
   for (int tb = 0; tb < L; tb += kCBlk) {
     const float2 cb = nb, cc = nc;
@@ -205,9 +221,18 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
     }
     acc = fmaf(Dv, xv, acc);
     if (GATE) acc *= silu(zv);
-    if (ev) Elem<TY>::st(static_cast<TY*>(p.y), ch * p.L + t, acc);
+    if (pend) {  // uniform
+      if (yok) Elem<TY>::st(static_cast<TY*>(p.y), ch * p.L + tpend, ypend);
+      if (ev) Elem<TY>::st(static_cast<TY*>(p.y), ch * p.L + t, acc);
+    } else {
+      ypend = acc;
+      yok = ev;
+      tpend = t;
+    }
+    pend = !pend;
     wave_lds_sync();  // the gathers are done before the next block's writes
   }
+  if (pend && yok) Elem<TY>::st(static_cast<TY*>(p.y), ch * p.L + tpend, ypend);
   if (p.h_final && chv && nv) {
     p.h_final[(ch * p.N + n) * 2] = hr;
     p.h_final[(ch * p.N + n) * 2 + 1] = hi;
@@ -327,6 +352,8 @@ ssm_status ssm_complex_scan_fwd(const ssm_scan_params* p, const void* x, const v
       !aligned(y, ys) || !aligned(A, 8) || (dt_bias && !aligned(dt_bias, 4)) || (Dskip && !aligned(Dskip, 4)) ||
       (h0 && !aligned(h0, 8)) || (h_final && !aligned(h_final, 8)))
     return fail(SSM_ERR_ALIGN, "a pointer is not aligned to its element size");
+  if ((p->dim + 15) / 16 * p->batch >= (int64_t(1) << 32))
+    return fail(SSM_ERR_SHAPE, "batch * ceil(dim / 16) reaches 2^32 workgroups");
   CScanArgs a{};
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z; a.h0 = h0; a.y = y;
   a.h_final = h_final; a.batch = p->batch; a.dim = p->dim; a.L = p->seqlen; a.N = static_cast<int>(p->dstate);
