@@ -164,22 +164,19 @@ def test_ssd_decode_bf16_output():
     assert torch.equal(yb.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
 
 
-def test_ssd_full_size_sampled_heads():
+def test_ssd_full_size():
     # the Mamba-2 2.7B layer at full size (4 x 4096, 80 heads of 64, N = 128), in the launch configuration the
-    # benchmark times; the oracle recomputes a sample of heads for every batch element
+    # benchmark times (three L-segments): every output and final state against the oracle (multithreaded)
     torch = G.torch_dev()
     w = I.SSD_WORKLOADS[1]
     d = I.ssd_inputs(w, with_h0=True)
     dd = G.to_dev(d)
     y, hf = run(dd)
-    yn, hn = G.to_np64(y), G.to_np64(hf)
-    for h in (0, 37, 79):
-        yr, hr = ref(d, heads=(h, h + 1))
-        ey = G.rel_max(yn[:, :, h:h + 1], yr)
-        eh = G.rel_max(hn[:, h:h + 1], hr)
-        print("full size head %d: y err %.2e, h err %.2e" % (h, ey, eh), flush=True)
-        assert ey <= TOL_SSD and eh <= TOL_SSD, (h, ey, eh)
     assert bool(torch.isfinite(y).all())
+    yr, hr = ref(d)
+    ey, eh = G.rel_max(G.to_np64(y), yr), G.rel_max(G.to_np64(hf), hr)
+    print("ssd full size: y err %.2e, h err %.2e" % (ey, eh), flush=True)
+    assert ey <= TOL_SSD and eh <= TOL_SSD, (ey, eh)
 
 
 @pytest.mark.parametrize("disc", [0, 1])
@@ -195,9 +192,9 @@ def test_ssd_zero_A_heads(disc):
     assert G.rel_max(G.to_np64(hf), hr) <= TOL_SSD
 
 
-def test_ssd_decode_full_size_sampled():
+def test_ssd_decode_full_size():
     """The decode step at the size the benchmark times (256 sequences x 80 heads of 64, N = 128, bf16 io, the 671 MB
-    fp32 state updated in place), two consecutive steps; the oracle recomputes a sample of sequences."""
+    fp32 state updated in place), two consecutive steps; every output and state value against the oracle."""
     torch = G.torch_dev()
     w = I.SSD_WORKLOADS[2]
     first = I.ssd_inputs(w, with_h0=True)
@@ -210,8 +207,8 @@ def test_ssd_decode_full_size_sampled():
         ys.append(ssm.ssd_state_update(st, dq["x"], dq["dt"], dq["A"], dq["B"], dq["C"], dt_bias=dq["dt_bias"],
                                        Dskip=dq["Dskip"], z=dq["z"], y_dtype=torch.float32))
     torch.cuda.synchronize()
-    sel = [0, 97, 255]
-    sr = h0[sel].astype(np.float64)
+    sel = slice(None)
+    sr = h0.astype(np.float64)
     for i, q in enumerate(steps):
         f = I.as_f64(q)
         fl = lambda k: None if f[k] is None else f[k][sel]
