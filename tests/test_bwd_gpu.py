@@ -123,6 +123,19 @@ def test_bwd_bf16_gradients_are_rne_of_fp32():
         assert torch.equal(g16[k], g32[k]), k
 
 
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_bwd_full_size(cfg):
+    """Full layer size (the 130M and 2.8B layers), the launch configuration the benchmark times, dy and dh_final
+    seeded normals everywhere: every gradient tensor against the oracle's backward on the whole layer."""
+    w = I.WORKLOADS[cfg]
+    d = I.scan_inputs(w, with_h0=True)
+    ct = I.cotangents(w, io=I.F32, with_dh_final=True)
+    g = run_bwd(G.to_dev(d), G.to_dev(ct))
+    ref = oracle_bwd(d, ct)
+    errs = compare(g, ref, TOL_BWD, w.name)
+    print("%s backward errors:" % w.name, {k: "%.1e" % e for k, e in errs.items()}, flush=True)
+
+
 @pytest.mark.parametrize("cfg,ndim", [(1, 6), (2, 6)])
 def test_bwd_full_size_sampled(cfg, ndim):
     """Full layer size, the launch configuration the benchmark times.  The backward is linear in dy, so with dy zero
