@@ -42,6 +42,7 @@ def hf_np(hf):
     (4, 1, 5, 1, 16, "f32", 1, False, False, True),
     (5, 3, 20, 130, 5, "bf16", 1, True, True, False),
     (6, 1, 40, 77, 1, "f32", 0, False, True, True),
+    (8, 3, 50, 90, 16, "bf16", 0, True, True, True),   # 12 workgroups: XCD runs of two and one tiles
 ])
 def test_complex_scan_random(seed, b, D, L, N, io, disc, gate, dskip, h0):
     d = small(seed, b, D, L, N, io, gate, dskip, h0)
