@@ -262,7 +262,8 @@ def ssd_algorithmic_flops(b, L, H, P, G, N, Q=64):
 
 
 # the source files each kernel is built from (its translation unit and the headers it includes)
-KERNEL_SOURCES = (("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
+KERNEL_SOURCES = (("scan_kernel<bf16,bf16,euler,gate,dskip,conv>", ("common.hpp", "scan_fwd.hpp", "ssm_conv_scan.hip")),
+                  ("scan_kernel", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
                   ("decode_", ("common.hpp", "scan_fwd.hpp", "ssm_scan.hip")),
                   ("bwd_", ("common.hpp", "ssm_scan_bwd.hip")),
                   ("ssd_", ("common.hpp", "ssm_ssd.hip")),
@@ -286,6 +287,14 @@ def src_hash(kernel_key):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def bwd_traffic():
+    """HBM bytes of one ssm_scan_bwd call on the 2.8B layer: prep, carry and main (the two reductions move under 1% of
+    it and have no record); None unless every record is current."""
+    parts = [measured_traffic("bwd_%s mamba2.8b-layer" % k)
+             for k in ("prep_kernel<bf16,bf16,euler,gate>", "carry_kernel", "main_kernel<bf16,bf16,euler,gate>")]
+    return None if any(v is None for v in parts) else sum(parts)
 
 
 def ssd_traffic(nseg):
@@ -640,7 +649,9 @@ def main():
         csl = slots + conv_algorithmic_slots(b, D, L, 4)
         out["conv_scan"] = {"workload": "mamba2.8b-layer + causal conv1d (width 4) + SiLU", "ms_per_step": cms,
                             "elements_per_s": elems / (cms * 1e-3), "overhead_vs_scan": cms / ms - 1.0,
-                            "roofline": alu_roofline(csl, cms, "scan_kernel<bf16,bf16,euler,gate,dskip,conv>"),
+                            "roofline": alu_roofline(csl, cms, "scan_kernel<bf16,bf16,euler,gate,dskip,conv>",
+                                                     measured_traffic("scan_kernel<bf16,bf16,euler,gate,dskip,conv> "
+                                                                      "mamba2.8b-layer")),
                             "algorithmic_bytes": nbytes + D * 4 * 5,
                             "note": "x is read once and the convolved sequence never goes to memory; a separate "
                                     "convolution kernel would add a write and a read of it (2 x 168 MB in bf16)"}
@@ -711,7 +722,8 @@ def main():
         out["complex_scan"] = {"workload": "mamba2.8b-layer shape, complex diagonal A (S4D-Lin), complex B, C",
                                "ms_per_step": xms, "elements_per_s": elems / (xms * 1e-3),
                                "ratio_to_real_scan": xms / ms,
-                               "roofline": alu_roofline(xsl, xms, "complex_scan_kernel mamba2.8b-layer")}
+                               "roofline": alu_roofline(xsl, xms, "complex_scan_kernel mamba2.8b-layer",
+                                                        measured_traffic("complex_scan_kernel mamba2.8b-layer"))}
 
     # ---- Mamba-2 SSD layer (scalar A per head, N = 128) at the Mamba-2 2.7B layer shape, bf16 matrix cores
     if not args.no_ssd:
@@ -856,7 +868,7 @@ def main():
         out["bwd"] = {"workload": "mamba2.8b-layer", "steps": args.bwd_steps, "ms_per_step": bms,
                       "elements_per_s": elems / (bms * 1e-3), "ratio_to_forward": bms / ms,
                       "kernels": "prep + carry + main + 2 reduce (one ssm_scan_bwd call)",
-                      "roofline": alu_roofline(bsl, bms, "ssm_scan_bwd (all five kernels)"),
+                      "roofline": alu_roofline(bsl, bms, "ssm_scan_bwd (all five kernels)", bwd_traffic()),
                       "algorithmic_bytes": bby, "achieved_GBps": bby / (bms * 1e-3) / 1e9,
                       "workspace_bytes": wsb_n,
                       "main_kernel_traffic": measured_traffic("bwd_main_kernel<bf16,bf16,euler,gate> mamba2.8b-layer")}
