@@ -6,22 +6,27 @@
 // parallel scan) is prior art; the design here is chosen for CDNA4's execution model:
 //
 //  * The work is ALU-bound on this chip, not HBM-bound: every (channel, step) needs N = 16 exponentials and ~4N FMAs
-//    for ~8 bytes of HBM traffic, while v_exp_f32 costs about two FMA issue slots.  So the kernel minimises VALU
-//    slots and balances them perfectly over the 1024 SIMDs.
+//    for ~8 bytes of HBM traffic, while v_exp_f32 takes four FMA issue slots and does not issue alongside them
+//    (measured by the issue-rate probe, issue_probe.hip).  So the kernel minimises VALU slots and balances them
+//    perfectly over the 1024 SIMDs.
 //  * One lane owns one (channel, n) state value: a 16-lane DPP row holds the 16 states of one channel, a wave four
 //    channels, a 256-thread workgroup sixteen channels.  Every lane runs the recurrence sequentially in time with its
 //    state in a VGPR; parallelism comes from channels x states, which needs no extra arithmetic (a time-parallel scan
 //    costs more VALU than it saves here).
 //  * Per step, Delta and Delta*x are per channel: lane j of the row computes them for step j of a 16-step block, and
-//    the scan reads them with DPP row_newbcast, which folds into the consuming v_mul at no cost.
+//    the scan reads them with DPP row_newbcast folded into the consuming v_mul (a DPP multiply issues at half the
+//    plain rate, still cheaper than any other way of getting the value into every lane).
 //  * B is staged per 64-step chunk in LDS as fp32 (converted once per workgroup, shared by its 16 channels).
 //  * The C-contraction y_t = sum_n C_n(t) h_n(t) is a transposition: each lane writes its 16 states of a block to LDS,
 //    then lane j of the row reads the 16 states of step j together with C(t) and does 16 FMAs, adds D x, applies the
 //    SiLU gate and stores y.  That lane is the same one that loaded x and z of step j, so no other data moves.
-//  * Long sequences with few channels (a million steps on 512 channels) are split into L-segments: a first pass
-//    computes every segment's zero-start end state and sum of Delta, a tiny pass chains them into carry-in states
-//    (exp(A * sum Delta) is the product of the segment's decays), and the main pass rescans each segment from its
-//    carry-in.
+//  * Long sequences with few channels (a million steps on 512 channels) are split into L-segments: one pass scans
+//    every segment at once (segment 0 from h0, the others from zero) and records end states and sums of Delta, a
+//    tiny pass chains them into carry-in states (exp(A * sum Delta) is the product of the segment's decays), and a
+//    correction pass adds the carry-in's part, which decays with the state's memory, over each segment's first
+//    steps only (a rescan of the rest where it has not yet died out).
+//  * Workgroups are ordered so that each XCD (with its own L2) takes a contiguous run of tiles: the workgroups that
+//    stage one batch element's B and C share an L2.
 #include "scan_fwd.hpp"
 
 #include <mutex>
