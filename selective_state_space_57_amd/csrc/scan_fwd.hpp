@@ -234,8 +234,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     if constexpr (PH != kHomog) *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
     *reinterpret_cast<float4*>(&sCt[ct][4 * cg]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
     __syncthreads();
+    // Full chunks issue the next chunk's loads unconditionally (past the last chunk they read zeros or neighbouring
+    // rows, unused): with the loads on one path only, the compiler's counter waits must hold for both paths, and at
+    // the chunk start it waited for nearly all of the just-issued staging loads.
     const bool more = t0 + kChunk < tend;  // uniform
-    if (more) fetch_staged(t0 + kChunk);
+    if (FULL || more) fetch_staged(t0 + kChunk);
 
     float ypend = 0.0f;  // full chunks: an even block's output, stored with the next block's
     static_assert((kChunk / kSub) % 2 == 0, "blocks are stored in pairs");
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       }
       const float uv = keep(ev, Buf<TI>::cvt(rd[s & 1]) + bias);
       const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s & 1])) : 0.0f;
-      if (tb + 2 * kSub < tend) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
+      if (FULL || tb + 2 * kSub < tend) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
       float delta = p.softplus ? softplus(uv) : uv;
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
