@@ -265,16 +265,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 
   auto quad0 = [&](int q) { return (static_cast<int64_t>(g) * p.Q + q) * 16 + w * 4; };  // first channel of a quad
   const uint32_t lane_off = static_cast<uint32_t>(r) * static_cast<uint32_t>(L) + static_cast<uint32_t>(n);
+  // This quad's A and dt bias are loaded a quad ahead, unconditionally and from valid addresses (an absent bias
+  // reads A), and masked where they are used: a load on one path only, or a value selected right after its load,
+  // makes the compiler wait for it (and for every load issued before it) on the spot.
+  const float* const biassrc = p.dt_bias ? p.dt_bias : p.A;
+  auto fetch_par = [&](int q, float& a, float& bi) {
+    int64_t dq = quad0(q) + r;
+    dq = dq < p.dim ? dq : 0;
+    a = p.A[dq * p.N + (nv ? n : 0)];
+    bi = biassrc[dq];
+  };
+  float a_nxt, bias_nxt;
+  fetch_par(0, a_nxt, bias_nxt);
   Owned<TI, TG> nxt = fetch_owned<TI, TG, GATE>(quad_io<TI, TG, GATE>(p, b, quad0(0)), r, lane_off + t0, t0 + n < L);
   for (int q = 0; q < p.Q; ++q) {
     const QuadIO<TI, TG> io = quad_io<TI, TG, GATE>(p, b, quad0(q));
     const int64_t d = quad0(q) + r;
     const bool chv = d < p.dim;
     const int64_t bd = b * p.dim + d;
-    const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
+    const float a_raw = a_nxt, bias_raw = bias_nxt;
+    fetch_par(q + 1, a_nxt, bias_nxt);  // past the last quad: an unused valid address
+    const float An = (chv && nv) ? a_raw : 0.0f;
     const float Ap = An * kLog2e;
     const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
-    const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
+    const float bias = (chv && p.dt_bias) ? bias_raw : 0.0f;
     const int64_t rec = bd * p.nck + k;
     float* const sp = p.side + rec * (kRec * kNP) + n;
     float* const cp = p.cum + rec * kNB;
@@ -434,26 +448,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   auto quad0 = [&](int q) { return (static_cast<int64_t>(g) * p.Q + q) * 16 + w * 4; };  // first channel of a quad
   auto chan = [&](int q) { return quad0(q) + r; };
   const uint32_t lane_off = static_cast<uint32_t>(r) * static_cast<uint32_t>(L) + static_cast<uint32_t>(n);
-  // per-quad carried values: h_in, rho, local block-start states and cumulative Delta of blocks 1..3
+  // Per-quad values: h_in, rho, the local block-start states and cumulative Delta of blocks 1..3, A, the dt bias and
+  // D.  They are loaded a quad ahead, unconditionally and from valid addresses (a quad past the last one or past dim
+  // reads channel 0; an absent bias or D reads A), and masked where they are used: a load on one path only, or a
+  // value selected right after its load, makes the compiler wait for it (and for every load issued before it) on the
+  // spot.
   struct Side {
-    float hin, rho, hl[kNB], cm[kNB];
+    float hin, rho, hl[kNB], cm[kNB], a, bias, dv;
   };
+  const float* const biassrc = p.dt_bias ? p.dt_bias : p.A;
+  const float* const dsrc = p.Dskip ? p.Dskip : p.A;
   auto fetch_side = [&](int q) {
     Side s;
-    const int64_t d = chan(q);
-    const bool ok = q < p.Q && d < p.dim;
-    const int64_t bd = b * p.dim + (ok ? d : 0);
-    const int64_t rec = bd * p.nck + k;
+    int64_t d = chan(q);
+    d = (q < p.Q && d < p.dim) ? d : 0;
+    const int64_t rec = (b * p.dim + d) * p.nck + k;
     const float* sp = p.side + rec * (kRec * kNP) + n;
     const float* cp = p.cum + rec * kNB;
-    s.hin = (ok && nv) ? p.sideE[rec * kNP + n] : 0.0f;
-    s.rho = (ok && nv) ? p.sideL[rec * kNP + n] : 0.0f;
+    s.hin = p.sideE[rec * kNP + n];
+    s.rho = p.sideL[rec * kNP + n];
     s.hl[0] = s.cm[0] = 0.0f;
 #pragma unroll
     for (int i = 1; i < kNB; ++i) {
-      s.hl[i] = (ok && nv) ? sp[(i - 1) * kNP] : 0.0f;
-      s.cm[i] = ok ? cp[i - 1] : 0.0f;
+      s.hl[i] = sp[(i - 1) * kNP];
+      s.cm[i] = cp[i - 1];
     }
+    s.a = p.A[d * p.N + (nv ? n : 0)];
+    s.bias = biassrc[d];
+    s.dv = dsrc[d];
     return s;
   };
 
@@ -471,13 +493,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     TG* const qdz = GATE ? static_cast<TG*>(p.dz) + obase : nullptr;
     const int64_t d = chan(q);
     const bool chv = d < p.dim;
-    const float An = (chv && nv) ? p.A[d * p.N + n] : 0.0f;
+    Side sd = side_nxt;
+    side_nxt = fetch_side(q + 1);
+    const bool sv = chv && nv;  // this lane's state exists
+    const float An = sv ? sd.a : 0.0f;
     const float Ap = An * kLog2e;
     const float rA = (ZOH && An != 0.0f) ? 1.0f / An : 0.0f;
-    const float bias = (chv && p.dt_bias) ? p.dt_bias[d] : 0.0f;
-    const float Dv = (chv && p.Dskip) ? p.Dskip[d] : 0.0f;
-    const Side sd = side_nxt;
-    side_nxt = fetch_side(q + 1);
+    const float bias = (chv && p.dt_bias) ? sd.bias : 0.0f;
+    const float Dv = (chv && p.Dskip) ? sd.dv : 0.0f;
+    sd.hin = sv ? sd.hin : 0.0f;
+    sd.rho = sv ? sd.rho : 0.0f;
+#pragma unroll
+    for (int i = 1; i < kNB; ++i) {
+      sd.hl[i] = sv ? sd.hl[i] : 0.0f;
+      sd.cm[i] = chv ? sd.cm[i] : 0.0f;
+    }
     float gam = sd.rho;  // adjoint entering the chunk's last step from later chunks
     const int boff = opaque(n * kSStride);
     float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
