@@ -152,20 +152,28 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
 
   // staging role: thread (sn = tid / 16, st = tid % 16) loads B, C of state sn at step tb + st
   const int sn = tid >> 4, st = tid & 15;
-  auto fetch = [&](int tb, float2& bv, float2& cv, float& xr, float& dr, float& zr) {
-    const int t = tb + st;
-    const bool okb = sn < p.N && t < L;
-    bv = okb ? ldc(Bp, static_cast<int64_t>(sn) * p.L + t) : make_float2(0.0f, 0.0f);
-    cv = okb ? ldc(Cp, static_cast<int64_t>(sn) * p.L + t) : make_float2(0.0f, 0.0f);
-    const int to = tb + n;  // the step this lane owns
-    const bool oko = chv && to < L;
-    xr = oko ? Elem<TI>::ld(X, ch * p.L + to) : 0.0f;
-    dr = oko ? Elem<TI>::ld(DT, ch * p.L + to) : 0.0f;
-    zr = (GATE && oko) ? Elem<TI>::ld(Z, ch * p.L + to) : 0.0f;
+  // A block's loads are issued a block ahead, unconditionally and from valid addresses (index 0 where the element
+  // lies outside the sequence, the state range or dim), and kept raw: conversion and masking happen at use.  A load on
+  // one path only, or a value converted or selected right after its load, makes the compiler wait for it (and for
+  // every load issued before it) on the spot.
+  struct Pre {
+    TI b0, b1, c0, c1, x, d, z;
   };
-  float2 nb, nc;
-  float nx, nd, nz;
-  fetch(0, nb, nc, nx, nd, nz);
+  auto fetch = [&](int tb, Pre& f) {
+    const int t = tb + st;
+    const int64_t ib = (sn < p.N && t < L) ? static_cast<int64_t>(sn) * p.L + t : 0;
+    f.b0 = Bp[2 * ib];
+    f.b1 = Bp[2 * ib + 1];
+    f.c0 = Cp[2 * ib];
+    f.c1 = Cp[2 * ib + 1];
+    const int to = tb + n;  // the step this lane owns
+    const int64_t io = (chv && to < L) ? ch * p.L + to : 0;
+    f.x = X[io];
+    f.d = DT[io];
+    f.z = GATE ? Z[io] : TI(0);
+  };
+  Pre nf;
+  fetch(0, nf);
   // the output of every other block waits for the next block's, so that the two 32-byte pieces of each row leave the
   // L2 together as one 64-byte write rather than as separate partial writes of one line
   float ypend = 0.0f;
@@ -173,15 +181,20 @@ __global__ __launch_bounds__(256) void complex_scan_kernel(CScanArgs p) {
   int tpend = 0;
 
   for (int tb = 0; tb < L; tb += kCBlk) {
-    const float2 cb = nb, cc = nc;
-    const float xv = nx, uv = nd + bias, zv = nz;
+    const Pre cf = nf;
     const int t = tb + n;
     const bool ev = chv && t < L;
+    const bool okb = sn < p.N && tb + st < L;
+    const float2 cb = okb ? make_float2(Elem<TI>::cvt(cf.b0), Elem<TI>::cvt(cf.b1)) : make_float2(0.0f, 0.0f);
+    const float2 cc = okb ? make_float2(Elem<TI>::cvt(cf.c0), Elem<TI>::cvt(cf.c1)) : make_float2(0.0f, 0.0f);
+    const float xv = ev ? Elem<TI>::cvt(cf.x) : 0.0f;
+    const float uv = (ev ? Elem<TI>::cvt(cf.d) : 0.0f) + bias;
+    const float zv = (GATE && ev) ? Elem<TI>::cvt(cf.z) : 0.0f;
     __syncthreads();  // the previous block's readers of sB / sC are done
     sB[sn][st] = cb;
     sC[sn][st] = cc;
     __syncthreads();
-    if (tb + kCBlk < L) fetch(tb + kCBlk, nb, nc, nx, nd, nz);
+    fetch(tb + kCBlk, nf);  // past the end: unused values from valid addresses
     float delta = p.softplus ? softplus(uv) : uv;
     delta = ev ? delta : 0.0f;  // padded steps: Abar = 1, Bbar = 0
     const float dxo = delta * xv;
