@@ -452,18 +452,22 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
   grows = fmaxf(grows, __shfl_xor(grows, 2, 16));
   grows = fmaxf(grows, __shfl_xor(grows, 1, 16));
   float h = nv ? E[ch * N + n] : 0.0f;
+  // a segment's records, raw: loaded unconditionally from valid addresses (state 0 for lanes beyond N) and masked
+  // where they are used, so that no wait for them sits at the load
   auto seg_in = [&](int s, float& e, float& hw, float& sum, float& sumw) {
-    const int64_t o = (static_cast<int64_t>(s) * bdN + ch) * N + n;
-    e = nv ? E[o] : 0.0f;
-    hw = nv ? HW[o] : 0.0f;
+    const int64_t o = (static_cast<int64_t>(s) * bdN + ch) * N + (nv ? n : 0);
+    e = E[o];
+    hw = HW[o];
     sum = S[s * bdN + ch];
     sumw = SW[s * bdN + ch];
   };
   float e = 0.0f, hw = 0.0f, sum = 0.0f, sumw = 0.0f;
   if (p.nseg > 1) seg_in(1, e, hw, sum, sumw);
   for (int s = 1; s < p.nseg; ++s) {
-    float e1 = 0.0f, hw1 = 0.0f, sum1 = 0.0f, sumw1 = 0.0f;
-    if (s + 1 < p.nseg) seg_in(s + 1, e1, hw1, sum1, sumw1);  // one segment ahead
+    float e1, hw1, sum1, sumw1;
+    seg_in(s + 1 < p.nseg ? s + 1 : s, e1, hw1, sum1, sumw1);  // one segment ahead (past the last: unused)
+    e = nv ? e : 0.0f;
+    hw = nv ? hw : 0.0f;
     const int64_t ts = static_cast<int64_t>(s) * p.seg_len;
     const int64_t te = ts + p.seg_len < p.L ? ts + p.seg_len : p.L;
     float cor = nv ? fabsf(hw_exp2(sumw * ap) * h) : 0.0f;
