@@ -609,26 +609,32 @@ __global__ void __launch_bounds__(256) ssd_decode_kernel(SsdDecodeArgs a) {
   const int h = static_cast<int>(bh % a.H);
   const int64_t b = bh / a.H;
   const int g = h / a.hpg;
+  const uint16_t* Bt = a.B + (b * a.G + g) * N;
+  const uint16_t* Ct = a.C + (b * a.G + g) * N;
+  float* srow = a.state + r * N;
+  f4 s[kV];
+  uint2 bw[kV], cw[kV];
+  // The state, B and C loads go first and unconditionally (a row past the end reads row 0, unused): a load on one
+  // path only makes the compiler wait for it on the spot, which kept one state load in flight per lane instead of
+  // all of them, behind the scalar loads of dt and x.
+#pragma unroll
+  for (int i = 0; i < kV; ++i) {
+    const int n0 = 4 * (q + 16 * i);
+    s[i] = *reinterpret_cast<const f4*>(srow + n0);
+    bw[i] = *reinterpret_cast<const uint2*>(Bt + n0);
+    cw[i] = *reinterpret_cast<const uint2*>(Ct + n0);
+  }
+  const uint16_t xraw = a.x[r];
+  const float draw = (a.Dskip ? a.Dskip : a.A)[h];  // an absent D or z reads another tensor, unused
+  const uint16_t zraw = (a.z ? a.z : a.x)[r];
   const float Ah = a.A[h];
   const float u = bf_lo(a.dt[bh]) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
   const float dl = a.softplus ? softplus(u) : u;
   const float e = dl * Ah;
   const float abar = hw_exp2(e * kLog2e);
   const float ph = ZOH ? (Ah == 0.0f ? dl : expm1_from(e, abar) / Ah) : dl;
-  const float xv = bf_lo(a.x[r]);
+  const float xv = bf_lo(xraw);
   const float bx = ph * xv;
-  const uint16_t* Bt = a.B + (b * a.G + g) * N;
-  const uint16_t* Ct = a.C + (b * a.G + g) * N;
-  float* srow = a.state + r * N;
-  f4 s[kV];
-  uint2 bw[kV], cw[kV];
-#pragma unroll
-  for (int i = 0; i < kV; ++i) {
-    const int n0 = 4 * (q + 16 * i);
-    s[i] = live ? *reinterpret_cast<const f4*>(srow + n0) : f4{0.0f, 0.0f, 0.0f, 0.0f};
-    bw[i] = *reinterpret_cast<const uint2*>(Bt + n0);
-    cw[i] = *reinterpret_cast<const uint2*>(Ct + n0);
-  }
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < kV; ++i) {
@@ -648,8 +654,8 @@ __global__ void __launch_bounds__(256) ssd_decode_kernel(SsdDecodeArgs a) {
   acc += row_ror<1>(acc);
   if (live && q == 0) {
     float yv = acc;
-    if (a.Dskip) yv = fmaf(a.Dskip[h], xv, yv);
-    if (a.z) yv *= silu(bf_lo(a.z[r]));
+    if (a.Dskip) yv = fmaf(draw, xv, yv);
+    if (a.z) yv *= silu(bf_lo(zraw));
     Elem<TY>::st(static_cast<TY*>(a.y), r, yv);
   }
 }
