@@ -60,6 +60,14 @@ def scan_algorithmic_slots(b, D, L, N, gate=True, dskip=True, softplus=True):
     return float(scan_elem_slots(N, gate, dskip, softplus)) * b * D * L
 
 
+def zoh_elem_slots(N, gate=True, dskip=True, softplus=True):
+    """The forward scan under the ZOH rule, per (b, d, t) element: Euler's slots plus, per state, the coefficient
+    expm1(Delta A) / A: Delta*A (1), expm1 near 0 as a degree-7 polynomial (7 FMA + 1 multiply), the choice between it
+    and exp - 1 (compare, select, subtract: 3), the division by A as a multiply (1), and B*x no longer sharing the
+    per-element Delta*x (1)."""
+    return scan_elem_slots(N, gate, dskip, softplus) + (1 + 8 + 3 + 1 + 1) * N
+
+
 def complex_algorithmic_slots(b, D, L, N, gate=True, dskip=True):
     """Complex-A forward per (b, d, t): per state Delta*Re(A), exp, sin + cos (about 18 fused multiply-adds and bit
     operations of the polynomial evaluation with its reduction), (Delta x) B (2), the complex update (4), Re(C h) (2)
@@ -440,6 +448,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-complex", action="store_true")
+    ap.add_argument("--no-zoh", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--no-configs", action="store_true", help="skip the legs of the other scan workloads")
@@ -690,6 +699,38 @@ def main():
                              "frac": gbs_ / HBM_PEAK_GBS,
                              "traffic": measured_traffic("conv1d_%s_kernel<bf16,bf16,4> mamba2.8b-layer" % name)}}
         del uu, gdx
+
+    # ---- the same forward under the ZOH rule, Bbar = expm1(Delta A) / A * B
+    if not args.no_zoh:
+        from selective_state_space_57_amd import _abi
+        pz = ssm.make_params(b, D, L, N, ssm.SSM_BF16, ssm.SSM_BF16, disc=ssm.ZOH)
+        zws_n = ssm.workspace_bytes(pz)
+        zws = torch.empty(max(zws_n, 1), dtype=torch.uint8, device=dev)
+        zargs = sargs[:-3] + (zws.data_ptr() if zws_n else 0, zws_n, stream.cuda_stream)
+
+        def zstep():
+            st = _abi.scan_fwd_raw(pz, *zargs)
+            if st:
+                _abi.check(st)
+
+        spin_up(torch, stream, zstep)
+        for _ in range(5):
+            zstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            zstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        zms = e0.elapsed_time(e1) / args.steps
+        zsl = float(zoh_elem_slots(N)) * elems
+        out["zoh"] = {"workload": "mamba2.8b-layer, ZOH rule for Bbar", "ms_per_step": zms,
+                      "elements_per_s": elems / (zms * 1e-3), "ratio_to_euler": zms / ms,
+                      "slots_per_element": zoh_elem_slots(N),
+                      "roofline": alu_roofline(zsl, zms, "scan_kernel<bf16,bf16,zoh,gate,dskip> mamba2.8b-layer",
+                                               None, {"hbm_frac": nbytes / (zms * 1e-3) / 1e9 / HBM_PEAK_GBS})}
+        del zws
 
     # ---- complex diagonal A (S4D-Lin) on the same shape: complex B, C and state
     if not args.no_complex:

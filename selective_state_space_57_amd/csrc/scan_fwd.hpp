@@ -71,8 +71,9 @@ constexpr int kCorrWindow = 2048;
 // Delta and Delta*x, contracting with C and storing y, plus four B and four C values it stages into LDS.  All of
 // these global loads are issued one chunk ahead, so their latency hides behind a whole chunk of arithmetic.
 template <typename TI, typename TY, bool ZOH, int MODE, bool GATE, bool DSKIP, bool CONV>
-// five resident workgroups per CU (<= 96 VGPRs): a 4 x 5120-channel layer is exactly 5 workgroups per CU
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void scan_kernel(ScanArgs p) {
+// five resident workgroups per CU (<= 96 VGPRs): a 4 x 5120-channel layer is exactly 5 workgroups per CU.  Under ZOH
+// four (<= 128 VGPRs): its coefficient expm1(Delta A)/A per state and step does not fit 96 registers without spills.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZOH ? 4 : 5, 8))) void scan_kernel(ScanArgs p) {
   __shared__ __align__(16) float sB[kChanPerWG][kBStride];     // B_n(t) of the chunk, [n][t]
   __shared__ __align__(16) float sCt[kChunk][kCtStride];       // C_n(t) of the chunk, [t][n]
   __shared__ __align__(16) float sH[kChanPerWG * kHRow];       // states of a 16-step block, per row [t][n]
@@ -234,11 +235,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     if constexpr (PH != kHomog) *reinterpret_cast<float4*>(&sB[nn][4 * q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
     *reinterpret_cast<float4*>(&sCt[ct][4 * cg]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
     __syncthreads();
-    // Full chunks issue the next chunk's loads unconditionally (past the last chunk they read zeros or neighbouring
-    // rows, unused): with the loads on one path only, the compiler's counter waits must hold for both paths, and at
-    // the chunk start it waited for nearly all of the just-issued staging loads.
+    // Full chunks issue the next chunk's loads unconditionally (after the last chunk they re-read this one, which
+    // the cache still holds, and are not used): with the loads on one path only, the compiler's counter waits must
+    // hold for both paths, and at the chunk start it waited for nearly all of the just-issued staging loads.
     const bool more = t0 + kChunk < tend;  // uniform
-    if (FULL || more) fetch_staged(t0 + kChunk);
+    if (FULL || more) fetch_staged(more ? t0 + kChunk : t0);
 
     float ypend = 0.0f;  // full chunks: an even block's output, stored with the next block's
     static_assert((kChunk / kSub) % 2 == 0, "blocks are stored in pairs");
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
       }
       const float uv = keep(ev, Buf<TI>::cvt(rd[s & 1]) + bias);
       const float zv = GATE ? keep(ev, Buf<TI>::cvt(rz[s & 1])) : 0.0f;
-      if (FULL || tb + 2 * kSub < tend) fetch_owned(tb + 2 * kSub, s & 1);  // uniform
+      if (FULL || tb + 2 * kSub < tend) fetch_owned(tb + 2 * kSub < tend ? tb + 2 * kSub : tb, s & 1);  // uniform
       float delta = p.softplus ? softplus(uv) : uv;
       delta = keep(ev, delta);  // padded steps: Abar = 1, Bbar = 0 -> the state is unchanged
       const float dx = delta * xv;
@@ -828,10 +829,12 @@ Plan make_plan(const ssm_scan_params* p, size_t max_ws = 0) {
     nseg = p->segments;
   } else {
     // fill the 1024 SIMDs: one wave per 4 channels; aim for 5120 waves (the five per SIMD that the kernel's 96
-    // registers allow), but keep segments >= 1024 steps
+    // registers allow; 4096 under ZOH, whose kernel takes 128 registers, four waves per SIMD), but keep segments
+    // >= 1024 steps
     const int64_t waves = ((p->dim + 15) / 16) * p->batch * 4;
+    const int64_t target = p->disc == SSM_DISC_ZOH ? 4096 : 5120;
     if (waves < 2048) {
-      nseg = (5120 + waves - 1) / waves;
+      nseg = (target + waves - 1) / waves;
       const int64_t maxseg = (p->seqlen + 1023) / 1024;
       if (nseg > maxseg) nseg = maxseg;
     }
