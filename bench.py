@@ -729,7 +729,9 @@ def main():
                       "elements_per_s": elems / (zms * 1e-3), "ratio_to_euler": zms / ms,
                       "slots_per_element": zoh_elem_slots(N),
                       "roofline": alu_roofline(zsl, zms, "scan_kernel<bf16,bf16,zoh,gate,dskip> mamba2.8b-layer",
-                                               None, {"hbm_frac": nbytes / (zms * 1e-3) / 1e9 / HBM_PEAK_GBS})}
+                                               measured_traffic("scan_kernel<bf16,bf16,zoh,gate,dskip> "
+                                                                "mamba2.8b-layer"),
+                                               {"hbm_frac": nbytes / (zms * 1e-3) / 1e9 / HBM_PEAK_GBS})}
         del zws
 
     # ---- complex diagonal A (S4D-Lin) on the same shape: complex B, C and state
