@@ -124,6 +124,15 @@ def test_workspace_query_and_errors(lib):
     assert _abi.workspace_bytes(P(dim=0)) == 0 and _abi.plan_segments(P(dim=0)) == 0
 
 
+def test_segment_plan_targets_the_resident_waves(lib):
+    # 512 channels = 128 waves; segments fill the waves the kernel keeps resident: five per SIMD (5120) under Euler-B,
+    # four (4096) under ZOH, whose kernel takes 128 registers
+    assert _abi.plan_segments(P(batch=1, dim=512, seqlen=1 << 20)) == 40
+    assert _abi.plan_segments(P(batch=1, dim=512, seqlen=1 << 20, disc=_abi.ZOH)) == 32
+    # never below 1024 steps per segment
+    assert _abi.plan_segments(P(batch=1, dim=512, seqlen=8192)) == 8
+
+
 def test_state_update_errors(lib):
     p = P(seqlen=0)  # seqlen is ignored by decode
     args = [FAKE] * 6 + [0, 0, FAKE, 0, 0]  # state, x, dt, (bias 0)...

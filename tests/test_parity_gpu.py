@@ -153,6 +153,34 @@ def test_layer_workload_full(cfg):
     assert np.array_equal(y16.to(torch.float32).cpu().numpy(), G.bf16_rne(y.cpu().numpy()))
 
 
+def test_million_length_zoh_sampled():
+    """The million-step layer under ZOH through the planner (32 segments: the ZOH kernel keeps four waves per SIMD
+    resident), in the launch configuration the benchmark times for its Euler leg: two blocks of 64 channels (the first
+    and the last workgroups' channels) against the oracle run on them, every output and final state."""
+    torch = G.torch_dev()
+    import selective_state_space_57_amd as ssm
+    ZOH = ssm.ZOH
+    w = I.WORKLOADS[3]
+    assert ssm.plan_segments(ssm.make_params(w.batch, w.dim, w.seqlen, w.dstate, ssm.SSM_BF16, disc=ssm.ZOH)) == 32
+    print("million-length ZOH: generating inputs", flush=True)
+    d = I.scan_inputs(w)
+    y, hf = G.run_gpu(G.to_dev(d), disc=ZOH, y_dtype=torch.float32)
+    yg = y.cpu().numpy()
+    hg = hf.cpu().numpy().astype(np.float64)
+    del y
+    for c0 in (0, w.dim - 64):
+        sub = {k: v for k, v in d.items()}
+        for k in ("x", "dt", "z"):
+            sub[k] = d[k][:, c0:c0 + 64]
+        for k in ("A", "dt_bias", "Dskip"):
+            sub[k] = d[k][c0:c0 + 64]
+        yr, hr = G.oracle_ref(sub, disc=ZOH)
+        ey = G.rel_max(yg[:, c0:c0 + 64].astype(np.float64), yr)
+        eh = G.rel_max(hg[:, c0:c0 + 64], hr)
+        print("million-length ZOH: channels %d..%d: err y %.3e h %.3e (of rms)" % (c0, c0 + 63, ey, eh), flush=True)
+        assert ey <= G.TOL_BF16 and eh <= G.TOL_BF16, (c0, ey, eh)
+
+
 def test_million_length_full_and_16_segment_handoff():
     # one batch element, 512 channels, 2^20 steps: the planner's segmented path (segments pass, carry, correction).
     # Every output and final state is compared with the oracle, 64 channels at a time (fp64 copies of one block
