@@ -64,6 +64,21 @@ enum ChunkPhase : int { kFullInput = 0, kWindowOut = 1, kHomog = 2 };
 // steps of each segment whose outputs the correction pass completes (a multiple of the 64-step chunk)
 constexpr int kCorrWindow = 2048;
 
+// ZOH input coefficient expm1(Delta A) / A from e = Delta A, a = exp(e) and rA = 1 / A: near 0 (|e| < 1/4) Delta
+// times the series of expm1(e) / e through e^6 / 7! (truncation below 2e-9 relative; at A = 0 it is Delta, the
+// rule's limit), elsewhere (a - 1) / A, where a - 1 loses no accuracy (A != 0 there).  Both are formed and one is
+// selected, so the lanes do not diverge.
+__device__ __forceinline__ float zoh_coef(float delta, float e, float a, float rA) {
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, e, 1.0f / 720.0f);
+  p = fmaf(p, e, 1.0f / 120.0f);
+  p = fmaf(p, e, 1.0f / 24.0f);
+  p = fmaf(p, e, 1.0f / 6.0f);
+  p = fmaf(p, e, 0.5f);
+  p = fmaf(p, e, 1.0f);
+  return fabsf(e) < 0.25f ? delta * p : (a - 1.0f) * rA;
+}
+
 // ---------------------------------------------------------------------------------------------------------------
 // The scan kernel (see ScanMode for the segment passes).
 //
@@ -322,9 +337,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZOH ? 
         } else {
           float bb;
           if (ZOH) {
-            const float en = dk * An;
-            const float coef = An != 0.0f ? expm1_from(en, a) * rA : dk;
-            bb = coef * bq[k] * row_bcast<k>(xv);
+            bb = zoh_coef(dk, dk * An, a, rA) * bq[k] * row_bcast<k>(xv);
           } else {
             bb = row_bcast<k>(dx) * bq[k];
           }
@@ -625,9 +638,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
       const float a = hw_exp2(delta * (As[i] * kLog2e));
       float bbar;
       if (ZOH) {
-        const float en = delta * As[i];
-        const float coef = As[i] != 0.0f ? expm1_from(en, a) * (1.0f / As[i]) : delta;
-        bbar = coef * Bv[j][i] * xv[j];
+        bbar = zoh_coef(delta, delta * As[i], a, 1.0f / As[i]) * Bv[j][i] * xv[j];
       } else {
         bbar = dx * Bv[j][i];
       }
@@ -744,9 +755,7 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeArgs p, int64_t g
         const float a = hw_exp2(delta * (As[i] * kLog2e));
         float bbar;
         if (ZOH) {
-          const float en = delta * As[i];
-          const float coef = As[i] != 0.0f ? expm1_from(en, a) * (1.0f / As[i]) : delta;
-          bbar = coef * Bv[i] * xv;
+          bbar = zoh_coef(delta, delta * As[i], a, 1.0f / As[i]) * Bv[i] * xv;
         } else {
           bbar = dx * Bv[i];
         }
