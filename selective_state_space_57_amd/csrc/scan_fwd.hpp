@@ -87,7 +87,8 @@ __device__ __forceinline__ float zoh_coef(float delta, float e, float a, float r
 // these global loads are issued one chunk ahead, so their latency hides behind a whole chunk of arithmetic.
 template <typename TI, typename TY, bool ZOH, int MODE, bool GATE, bool DSKIP, bool CONV>
 // five resident workgroups per CU (<= 96 VGPRs): a 4 x 5120-channel layer is exactly 5 workgroups per CU.  Under ZOH
-// four (<= 128 VGPRs): its coefficient expm1(Delta A)/A per state and step does not fit 96 registers without spills.
+// at least four (<= 128 VGPRs): the segmented passes' ZOH variants need up to 108 registers for the coefficient
+// expm1(Delta A)/A per state and step (the whole-sequence one fits 96).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZOH ? 4 : 5, 8))) void scan_kernel(ScanArgs p) {
   __shared__ __align__(16) float sB[kChanPerWG][kBStride];     // B_n(t) of the chunk, [n][t]
   __shared__ __align__(16) float sCt[kChunk][kCtStride];       // C_n(t) of the chunk, [t][n]
@@ -838,8 +839,8 @@ Plan make_plan(const ssm_scan_params* p, size_t max_ws = 0) {
     nseg = p->segments;
   } else {
     // fill the 1024 SIMDs: one wave per 4 channels; aim for 5120 waves (the five per SIMD that the kernel's 96
-    // registers allow; 4096 under ZOH, whose kernel takes 128 registers, four waves per SIMD), but keep segments
-    // >= 1024 steps
+    // registers allow; 4096 under ZOH, whose segmented passes take up to 108 registers, four waves per SIMD), but
+    // keep segments >= 1024 steps
     const int64_t waves = ((p->dim + 15) / 16) * p->batch * 4;
     const int64_t target = p->disc == SSM_DISC_ZOH ? 4096 : 5120;
     if (waves < 2048) {

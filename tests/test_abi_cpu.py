@@ -126,7 +126,7 @@ def test_workspace_query_and_errors(lib):
 
 def test_segment_plan_targets_the_resident_waves(lib):
     # 512 channels = 128 waves; segments fill the waves the kernel keeps resident: five per SIMD (5120) under Euler-B,
-    # four (4096) under ZOH, whose kernel takes 128 registers
+    # four (4096) under ZOH, whose segmented passes take more than 96 registers
     assert _abi.plan_segments(P(batch=1, dim=512, seqlen=1 << 20)) == 40
     assert _abi.plan_segments(P(batch=1, dim=512, seqlen=1 << 20, disc=_abi.ZOH)) == 32
     # never below 1024 steps per segment
