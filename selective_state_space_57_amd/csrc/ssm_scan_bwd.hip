@@ -85,6 +85,20 @@ struct BwdArgs {
 
 __device__ __forceinline__ float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 
+// ZOH input coefficient expm1(Delta A) / A from e = Delta A, a = exp(e) and rA = 1 / A: near 0 (|e| < 1/4) Delta
+// times the series of expm1(e) / e through e^6 / 7! (truncation below 2e-9 relative; Delta itself at A = 0), elsewhere
+// (a - 1) / A, where A != 0.  Both are formed and one is selected, so the lanes do not diverge.
+__device__ __forceinline__ float zoh_coef(float delta, float e, float a, float rA) {
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, e, 1.0f / 720.0f);
+  p = fmaf(p, e, 1.0f / 120.0f);
+  p = fmaf(p, e, 1.0f / 24.0f);
+  p = fmaf(p, e, 1.0f / 6.0f);
+  p = fmaf(p, e, 0.5f);
+  p = fmaf(p, e, 1.0f);
+  return fabsf(e) < 0.25f ? delta * p : (a - 1.0f) * rA;
+}
+
 // Workgroup order of prep and main, whose grid is (chunk, channel group, batch).  Workgroups with consecutive linear
 // ids go to the eight XCDs in turn, each with its own L2; the linear id i is mapped to the tile that gives XCD i mod 8
 // a contiguous run of tiles, chunk fastest.  The chunks of one channel group then share an L2: their records of
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
         const float a = hw_exp2(dk * Ap);
         float bb;
         if constexpr (ZOH) {
-          const float coef = An != 0.0f ? expm1_from(dk * An, a) * rA : dk;
+          const float coef = zoh_coef(dk, dk * An, a, rA);
           bb = coef * bq[K] * row_bcast<K>(xb);
         } else {
           bb = row_bcast<K>(dxo) * bq[K];
@@ -553,7 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         const float a = hw_exp2(dk * Ap);
         float bb;
         if constexpr (ZOH) {
-          const float coef = An != 0.0f ? expm1_from(dk * An, a) * rA : dk;
+          const float coef = zoh_coef(dk, dk * An, a, rA);
           Cf[K] = coef;
           bb = coef * bq[K] * row_bcast<K>(xb);
         } else {
