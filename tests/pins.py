@@ -555,9 +555,7 @@ def pin_ssd(orc, seed=14):
         assert np.max(np.abs(st - hf)) < 1e-12, ("P14d state", disc)
 
 
-def all_pins(orc, worked_rows):
-    """Run every pin; returns a list of (name, error-or-None)."""
-    out = []
+def _checks(orc, worked_rows):
     checks = [("worked", lambda: pin_worked_examples(orc, worked_rows)), ("theorem1", lambda: pin_theorem1(orc)),
               ("zoh_euler", lambda: pin_zoh_euler(orc))]
     for disc in (EULER_B, ZOH):
@@ -573,10 +571,29 @@ def all_pins(orc, worked_rows):
     checks += [("conv_numpy", lambda: pin_conv_numpy(orc)), ("conv_split", lambda: pin_conv_split(orc)),
                ("conv_bwd_fd", lambda: pin_conv_bwd_finite_differences(orc)),
                ("complex", lambda: pin_complex(orc)), ("ssd", lambda: pin_ssd(orc))]
-    for name, fn in checks:
-        try:
-            fn()
-            out.append((name, None))
-        except Exception as e:  # noqa: BLE001 -- a mutant may also crash or raise
-            out.append((name, repr(e)[:200]))
-    return out
+    return checks
+
+
+def _run(fn):
+    try:
+        fn()
+        return None
+    except Exception as e:  # noqa: BLE001 -- a mutant may also crash or raise
+        return repr(e)[:200]
+
+
+def all_pins(orc, worked_rows):
+    """Run every pin; returns a list of (name, error-or-None)."""
+    return [(name, _run(fn)) for name, fn in _checks(orc, worked_rows)]
+
+
+def first_failure(orc, worked_rows, prefer=()):
+    """Run the pins until one fails, those whose names start with one of `prefer` first; returns (name, error), or
+    None when every pin passes.  A planted mistake has to fail one pin, and which one does not matter."""
+    checks = _checks(orc, worked_rows)
+    first = [c for c in checks if c[0].startswith(tuple(prefer))] if prefer else []
+    for name, fn in first + [c for c in checks if c not in first]:
+        err = _run(fn)
+        if err is not None:
+            return name, err
+    return None

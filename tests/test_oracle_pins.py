@@ -201,13 +201,19 @@ MUTANTS = [
 ]
 
 
+# the pins a mistake in each part of the oracle is likely to fail, tried first (every pin is tried before a mutant
+# counts as uncaught)
+PREFER = (("conv_bwd", ("conv_bwd_fd",)), ("conv", ("conv_numpy", "conv_split")), ("complex", ("complex",)),
+          ("ssd", ("ssd",)), ("bwd", ("bwd_fd",)), ("decode", ("decode_scan",)))
+
+
 @pytest.mark.parametrize("name,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_is_caught(name, pat, rep):
     src = oracle.source_text()
     mutated, n = re.subn(pat, rep, src)
     assert n >= 1, "mutation pattern %s no longer matches the oracle source" % name
+    prefer = next((p for k, p in PREFER if name.startswith(k)), ())
     with tempfile.TemporaryDirectory() as td:
         lib = oracle.compile_variant(mutated, os.path.join(td, "mut_%s.so" % name))
-        res = pins.all_pins(oracle.Oracle(lib), load_worked())
-    failed = [k for k, e in res if e is not None]
-    assert failed, "mutant %s passed every pin" % name
+        caught = pins.first_failure(oracle.Oracle(lib), load_worked(), prefer)
+    assert caught is not None, "mutant %s passed every pin" % name
