@@ -110,8 +110,9 @@ def test_softplus_tails(orc):
 
 
 def test_all_pins_run_and_pass(orc):
-    """The mutation test below relies on all_pins: every entry must be (name, None) for the true oracle, and every
-    family of pins must be in it (a check that is listed but never run would make the mutation test vacuous)."""
+    """The mutation test below runs the same list of pins (first_failure and all_pins share it): every entry must be
+    (name, None) for the true oracle, and every family of pins must be in it (a check that is listed but never run
+    would make the mutation test vacuous)."""
     res = pins.all_pins(orc, load_worked())
     assert all(isinstance(k, str) and e is None for k, e in res), [r for r in res if r[1] is not None]
     names = {k for k, _ in res}
